@@ -1,0 +1,189 @@
+"""Benchmark of the KDA chunked forward pass on one MI355X.
+
+One step = one ``kda_fwd`` call over the whole workload (every stage of the
+forward pass runs inside it), inputs already resident in HBM.  The default
+workload is the large throughput case: B=8, T=16384, H=32, K=V=128,
+lower_bound=-5, scale=1/sqrt(128), fp32 final_state written, no initial
+state.  Prints one JSON line:
+
+  value     head-tokens/s of the whole job (B*T*H per step / seconds per step)
+  roofline  the kernel against HBM: algorithmic bytes per launch (inputs read
+            once, outputs written once) / average launch time (HIP events on
+            the launch stream), against 8 TB/s
+  cpu_baseline  the fp64 CPU oracle timed on this host on a bounded sample of
+            the same workload (whole sequences of two batch rows)
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic_large_b8_t16384_h32.json")
+
+
+def source_digest() -> str:
+    """sha256 over the kernel sources, to tell whether stored counters apply."""
+    csrc = os.path.join(HERE, "gated_delta_rule_36_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".cpp", ".h")):
+            with open(os.path.join(csrc, name), "rb") as fh:
+                h.update(name.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def algorithmic_bytes(x, final_dtype) -> int:
+    """Bytes the method must move once: q, k, v, g, beta and out in bf16,
+    A_log and dt_bias, the states, cu_seqlens."""
+    B, T, H, K = x.q.shape
+    rows = B * T * H
+    n = rows * K * 2 * 4 + rows * 2 + rows * 128 * 2
+    n += (H * 4 if x.A_log is not None else 0) + (H * K * 4 if x.dt_bias is not None else 0)
+    chains = x.num_seqs * H
+    if x.initial_state is not None:
+        n += chains * 128 * 128 * x.initial_state.element_size()
+    if final_dtype is not None:
+        n += chains * 128 * 128 * (2 if str(final_dtype).endswith("bfloat16") else 4)
+    if x.cu_seqlens is not None:
+        n += x.cu_seqlens.numel() * 8
+    return n
+
+
+def stored_traffic(launch_bytes: int):
+    """HBM bytes per launch from committed rocprofv3 counters, if they were
+    taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(x, rows: int = 2):
+    """Time the oracle on whole sequences of the first `rows` batch rows."""
+    import torch
+    from oracle import kda_oracle
+    B, T, H, _ = x.q.shape
+    rows = min(rows, B) if x.cu_seqlens is None else 1
+    cores = min(16, len(os.sched_getaffinity(0)))
+    sl = slice(0, rows)
+    cpu = lambda t: None if t is None else t.cpu()
+    q, k, v, g, beta = (cpu(t[sl]) for t in (x.q, x.k, x.v, x.g, x.beta))
+    init = None if x.initial_state is None else cpu(x.initial_state[sl] if x.cu_seqlens is None
+                                                    else x.initial_state)
+    cu = cpu(x.cu_seqlens)
+    N = rows if cu is None else cu.numel() - 1
+    chains = [(n, h) for n in range(N) for h in range(H)]
+    t0 = time.perf_counter()
+    kda_oracle(q, k, v, g, beta, x.scale, cpu(x.A_log), cpu(x.dt_bias), x.lower_bound,
+               initial_state=init, cu_seqlens=cu, chains=chains, threads=cores)
+    dt = time.perf_counter() - t0
+    head_tokens = rows * T * H
+    return {"value": head_tokens / dt, "unit": "head-tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(chains)} whole (sequence, head) chains = {head_tokens} head-tokens "
+                      f"({rows} of {B} batch rows, all {H} heads), fp64 token loop, "
+                      f"{dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="large_b8_t16384_h32")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported; this path runs on one GPU "
+              "(every (sequence, head) chain is independent, see the design notes on "
+              "sharding)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_36_amd as kda
+    from gated_delta_rule_36_amd import synth
+
+    torch.cuda.set_device(0)
+    print(f"[bench] drawing {args.workload} on the GPU", file=sys.stderr, flush=True)
+    x = synth.workload(args.workload, device="cuda")
+    B, T, H, K = x.q.shape
+    final_dtype = x.final_dtype
+    out = torch.empty_like(x.v)
+    final = None
+    if final_dtype is not None:
+        final = torch.empty(x.num_seqs, H, 128, 128, dtype=final_dtype, device="cuda")
+    torch.cuda.synchronize()
+
+    def step():
+        kda.fwd(x.q, x.k, x.v, x.g, x.beta, x.scale, out, x.A_log, x.dt_bias, x.lower_bound,
+                initial_state=x.initial_state, final_state=final, cu_seqlens=x.cu_seqlens,
+                check_cu_seqlens=False)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        step()
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s.elapsed_time(e) for s, e in ev]
+    ms_per_step = wall * 1e3 / args.steps
+    head_tokens = B * T * H
+    print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr,
+          flush=True)
+
+    avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+    launch_bytes = algorithmic_bytes(x, final_dtype)
+    achieved = launch_bytes / avg_launch_s / 1e9
+    traffic = stored_traffic(launch_bytes)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel_ms": round(avg_launch_s * 1e3, 4), "bytes_per_launch": launch_bytes}
+
+    result = {
+        "metric": "KDA fwd head-tokens/sec (K=V=128); % of HBM/MFMA roofline",
+        "value": head_tokens / (ms_per_step / 1e3),
+        "unit": "head-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "T": T, "H": H, "K": K, "V": 128,
+                   "lower_bound": x.lower_bound, "varlen": x.cu_seqlens is not None,
+                   "initial_state": None if x.initial_state is None else str(x.initial_state.dtype),
+                   "final_state": None if final_dtype is None else str(final_dtype)},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(x)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

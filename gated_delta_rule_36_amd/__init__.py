@@ -1,0 +1,11 @@
+"""MI355X (gfx950) Kimi Delta Attention chunked forward pass.
+
+``fwd(...)`` is the whole API: a thin binding over the C-ABI library
+``libkda.so`` (declared in ``include/kda.h``), whose hand-written HIP kernels
+run every step of the forward pass.  ``synth`` draws the seeded synthetic
+inputs of the named workloads.
+"""
+from ._lib import KdaLibraryMissing
+from .api import KdaArgumentError, KdaError, fwd
+
+__all__ = ["fwd", "KdaError", "KdaArgumentError", "KdaLibraryMissing"]

@@ -1,0 +1,142 @@
+"""Python binding of the KDA forward library: ``fwd(...)``.
+
+Argument marshalling only.  Every step of the forward pass runs in the HIP
+kernels of ``libkda.so``; there is no other implementation to fall back on,
+so a missing library raises :class:`KdaLibraryMissing`.
+
+The call form and the tensor contract follow the FlashKDA input-tensor page
+("Complete Forward Pass Example" and the sections above it): bf16
+``[B,T,H,128]`` q/k/v/g/out, bf16 ``[B,T,H]`` beta logits, fp32 ``A_log [H]``
+and ``dt_bias [H,128]``, ``lower_bound`` in [-5, 0], optional bf16/fp32
+``[N,H,V,K]`` states and an optional int64 ``cu_seqlens [N+1]`` with B = 1.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+_STATE_CODES = {torch.bfloat16: _lib.KDA_DTYPE_BF16, torch.float32: _lib.KDA_DTYPE_FP32}
+
+
+class KdaError(RuntimeError):
+    """The library rejected a call; ``status`` holds the kda_status code."""
+
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"kda_fwd failed: {_lib.status_string(status)} (status {status})")
+
+
+class KdaArgumentError(KdaError, ValueError):
+    """An argument error reported by the library before any launch."""
+
+
+def _check_tensor(name, t, dtype, device, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+        beta: torch.Tensor, scale: float, out: torch.Tensor,
+        A_log: Optional[torch.Tensor], dt_bias: Optional[torch.Tensor],
+        lower_bound: float, initial_state: Optional[torch.Tensor] = None,
+        final_state: Optional[torch.Tensor] = None,
+        cu_seqlens: Optional[torch.Tensor] = None, *,
+        check_cu_seqlens: bool = True) -> torch.Tensor:
+    """Run the chunked KDA forward pass; writes ``out`` (and ``final_state``).
+
+    Enqueued on the current stream of ``q``'s device; returns ``out``.
+    ``check_cu_seqlens`` copies ``cu_seqlens`` to the host (a synchronising
+    copy) to check it is nondecreasing from 0 to T; the kernels never read
+    outside the tensors either way.
+    """
+    if not isinstance(q, torch.Tensor):
+        raise TypeError("q must be a torch.Tensor")
+    device = q.device
+    # dtypes first, so a wrong dtype is reported as such wherever it lives
+    for name, t, dt in (("q", q, torch.bfloat16), ("k", k, torch.bfloat16),
+                        ("v", v, torch.bfloat16), ("g", g, torch.bfloat16),
+                        ("beta", beta, torch.bfloat16), ("out", out, torch.bfloat16),
+                        ("A_log", A_log, torch.float32), ("dt_bias", dt_bias, torch.float32),
+                        ("cu_seqlens", cu_seqlens, torch.int64)):
+        if t is None and name in ("A_log", "dt_bias", "cu_seqlens"):
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype != dt:
+            raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+    for name, t in (("q", q), ("k", k), ("g", g)):
+        _check_tensor(name, t, torch.bfloat16, device, ndim=4)
+    _check_tensor("v", v, torch.bfloat16, device, ndim=4)
+    _check_tensor("out", out, torch.bfloat16, device, ndim=4)
+    _check_tensor("beta", beta, torch.bfloat16, device, ndim=3)
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    if k.shape != q.shape or g.shape != q.shape:
+        raise ValueError("q, k and g must share the shape [B,T,H,K]")
+    if v.shape[:3] != q.shape[:3] or out.shape != v.shape:
+        raise ValueError("v and out must be [B,T,H,V] with q's B, T, H")
+    if beta.shape != q.shape[:3]:
+        raise ValueError("beta must be [B,T,H]")
+    if A_log is not None:
+        _check_tensor("A_log", A_log, torch.float32, device, ndim=1)
+        if A_log.shape != (H,):
+            raise ValueError("A_log must be [H]")
+    if dt_bias is not None:
+        _check_tensor("dt_bias", dt_bias, torch.float32, device, ndim=2)
+        if dt_bias.shape != (H, K):
+            raise ValueError("dt_bias must be [H,K]")
+
+    num_seqs = 0
+    if cu_seqlens is not None:
+        _check_tensor("cu_seqlens", cu_seqlens, torch.int64, device, ndim=1)
+        if cu_seqlens.numel() < 1:
+            raise ValueError("cu_seqlens must have N+1 >= 1 entries")
+        num_seqs = cu_seqlens.numel() - 1
+        if check_cu_seqlens:
+            host = cu_seqlens.cpu()
+            if int(host[0]) != 0 or int(host[-1]) != T or bool((host[1:] < host[:-1]).any()):
+                raise ValueError("cu_seqlens must be nondecreasing from 0 to T")
+    N = num_seqs if cu_seqlens is not None else B
+
+    codes = []
+    for name, st in (("initial_state", initial_state), ("final_state", final_state)):
+        if st is None:
+            codes.append(_lib.KDA_DTYPE_NONE)
+            continue
+        if st.dtype not in _STATE_CODES:
+            raise TypeError(f"{name} must be bfloat16 or float32, got {st.dtype}")
+        _check_tensor(name, st, st.dtype, device, ndim=4)
+        if st.shape != (N, H, V, K):
+            raise ValueError(f"{name} must be [N,H,V,K] = {(N, H, V, K)}, got {tuple(st.shape)}")
+        codes.append(_STATE_CODES[st.dtype])
+
+    lib = _lib.load()
+    with torch.cuda.device(device):
+        stream = torch.cuda.current_stream(device).cuda_stream
+        status = lib.kda_fwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(out),
+            _ptr(A_log), _ptr(dt_bias), float(lower_bound),
+            _ptr(initial_state), codes[0], _ptr(final_state), codes[1],
+            _ptr(cu_seqlens), num_seqs, B, T, H, K, V, stream)
+    if status != _lib.KDA_OK:
+        if status == _lib.KDA_ERR_LAUNCH:
+            raise KdaError(status)
+        raise KdaArgumentError(status)
+    return out

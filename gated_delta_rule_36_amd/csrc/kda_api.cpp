@@ -1,0 +1,148 @@
+// C-ABI front end of the KDA forward library: argument checks, the log2 gate
+// scale, and the hand-off to the kernels.  Every check runs on the host
+// before anything is enqueued; nothing here touches device memory.
+#include "kda.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "kda_internal.h"
+
+namespace {
+
+constexpr double kLog2e = 1.4426950408889634;  // 1 / ln 2
+
+bool mul_ok(int64_t a, int64_t b, int64_t *r) { return !__builtin_mul_overflow(a, b, r); }
+
+// Byte range [lo, hi) of a buffer.
+struct Span {
+    uintptr_t lo = 0, hi = 0;
+    bool overlaps(const Span &o) const { return lo < o.hi && o.lo < hi; }
+};
+
+Span span(const void *p, int64_t bytes)
+{
+    Span s;
+    if (p && bytes > 0) {
+        s.lo = reinterpret_cast<uintptr_t>(p);
+        s.hi = s.lo + static_cast<uintptr_t>(bytes);
+    }
+    return s;
+}
+
+bool valid_kind(kda_dtype d) { return d == KDA_DTYPE_BF16 || d == KDA_DTYPE_FP32; }
+
+}  // namespace
+
+extern "C" kda_status kda_fwd(const void *q, const void *k, const void *v, const void *g,
+                              const void *beta, double scale, void *out, const float *A_log,
+                              const float *dt_bias, double lower_bound,
+                              const void *initial_state, kda_dtype initial_state_dtype,
+                              void *final_state, kda_dtype final_state_dtype,
+                              const int64_t *cu_seqlens, int64_t num_seqs, int64_t B,
+                              int64_t T, int64_t H, int64_t K, int64_t V, void *stream)
+{
+    if (K != kda::kHeadDim || V != kda::kHeadDim)
+        return KDA_ERR_HEAD_DIM;
+    // NaN fails both comparisons and is rejected too.
+    if (!(lower_bound >= -5.0 && lower_bound <= 0.0))
+        return KDA_ERR_LOWER_BOUND;
+    if (!std::isfinite(scale))
+        return KDA_ERR_SCALE;
+    if (B < 1 || H < 1 || T < 0)
+        return KDA_ERR_SIZE;
+    if (cu_seqlens && (B != 1 || num_seqs < 0))
+        return KDA_ERR_VARLEN_BATCH;
+    if (initial_state && !valid_kind(initial_state_dtype))
+        return initial_state_dtype == KDA_DTYPE_NONE ? KDA_ERR_NULL_POINTER : KDA_ERR_STATE_DTYPE;
+    if (final_state && !valid_kind(final_state_dtype))
+        return final_state_dtype == KDA_DTYPE_NONE ? KDA_ERR_NULL_POINTER : KDA_ERR_STATE_DTYPE;
+    if (initial_state && final_state && initial_state_dtype != final_state_dtype)
+        return KDA_ERR_STATE_DTYPE;
+
+    const int64_t N = cu_seqlens ? num_seqs : B;
+    // rows = B*T*H token-head rows; act_bytes = bytes of one bf16 [B,T,H,128]
+    // tensor; state_f32_bytes = bytes of an fp32 [N,H,128,128] state.
+    int64_t tokens, rows, act_bytes, beta_bytes, chains, state_f32_bytes;
+    if (!mul_ok(B, T, &tokens) || !mul_ok(tokens, H, &rows) ||
+        !mul_ok(rows, 128 * 2, &act_bytes) || !mul_ok(rows, 2, &beta_bytes) ||
+        !mul_ok(N, H, &chains) || !mul_ok(chains, 128 * 128 * 4, &state_f32_bytes) ||
+        chains > INT32_MAX)
+        return KDA_ERR_SIZE;
+    // Token tensors may be NULL only when they are empty (T == 0).
+    if (rows > 0 && (!q || !k || !v || !g || !beta || !out))
+        return KDA_ERR_NULL_POINTER;
+    const int64_t init_bytes =
+        initial_state ? state_f32_bytes / (initial_state_dtype == KDA_DTYPE_BF16 ? 2 : 1) : 0;
+    const int64_t final_bytes =
+        final_state ? state_f32_bytes / (final_state_dtype == KDA_DTYPE_BF16 ? 2 : 1) : 0;
+
+    const Span inputs[] = {span(q, act_bytes), span(k, act_bytes), span(v, act_bytes),
+                           span(g, act_bytes), span(beta, beta_bytes),
+                           span(A_log, A_log ? H * 4 : 0), span(dt_bias, dt_bias ? H * 512 : 0),
+                           span(cu_seqlens, cu_seqlens ? (N + 1) * 8 : 0)};
+    const Span so = span(out, act_bytes), sf = span(final_state, final_bytes),
+               si = span(initial_state, init_bytes);
+    for (const Span &s : inputs) {
+        if (so.overlaps(s) || sf.overlaps(s))
+            return KDA_ERR_ALIAS;
+    }
+    if (so.overlaps(sf) || so.overlaps(si))
+        return KDA_ERR_ALIAS;
+    if (sf.overlaps(si) && final_state != initial_state)
+        return KDA_ERR_ALIAS;
+
+    if (chains == 0)
+        return KDA_OK;
+
+    kda::FwdParams p;
+    p.q = static_cast<const uint16_t *>(q);
+    p.k = static_cast<const uint16_t *>(k);
+    p.v = static_cast<const uint16_t *>(v);
+    p.g = static_cast<const uint16_t *>(g);
+    p.beta = static_cast<const uint16_t *>(beta);
+    p.out = static_cast<uint16_t *>(out);
+    p.A_log = A_log;
+    p.dt_bias = dt_bias;
+    p.init_state = initial_state;
+    p.final_state = final_state;
+    p.init_kind = initial_state ? static_cast<int>(initial_state_dtype) : kda::kStateNone;
+    p.final_kind = final_state ? static_cast<int>(final_state_dtype) : kda::kStateNone;
+    p.cu_seqlens = cu_seqlens;
+    p.num_seqs = N;
+    p.T = T;
+    p.H = H;
+    p.scale = static_cast<float>(scale);
+    // The gate is carried in log2 units so that every decay is a plain exp2
+    // (lower_bound page, "Conversion to the Gate Scale Factor").
+    p.gate_scale = static_cast<float>(lower_bound * kLog2e);
+
+    hipError_t err = kda::launch_forward(p, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+extern "C" const char *kda_status_string(kda_status status)
+{
+    switch (status) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL_POINTER: return "a required pointer is NULL (or a state has no dtype)";
+    case KDA_ERR_HEAD_DIM: return "K and V must both be 128";
+    case KDA_ERR_LOWER_BOUND: return "lower_bound must lie in [-5, 0]";
+    case KDA_ERR_VARLEN_BATCH: return "cu_seqlens requires B == 1 and num_seqs >= 0";
+    case KDA_ERR_STATE_DTYPE: return "state dtype must be bf16 or fp32, and match between initial and final";
+    case KDA_ERR_ALIAS: return "an output buffer overlaps an input buffer";
+    case KDA_ERR_SIZE: return "bad size (B, H >= 1, T >= 0, no int64 overflow)";
+    case KDA_ERR_SCALE: return "scale must be finite";
+    case KDA_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
+    }
+    return "unknown status";
+}
+
+extern "C" int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+namespace kda {
+hipError_t launch_forward(const FwdParams &p, hipStream_t stream)
+{
+    return launch_chunk_simt(p, stream);
+}
+}  // namespace kda

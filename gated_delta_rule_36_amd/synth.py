@@ -7,9 +7,11 @@ their inputs from here.
 Recipe (the same for every workload; the pages run no dataset or public
 benchmark, so every input is synthetic):
 
-* a CPU ``torch.Generator`` seeded with ``seed`` (0 unless stated), drawn in
-  the fixed order: [sequence lengths], q, k, v, g, beta logits, A_log,
-  dt_bias, [initial_state];
+* a ``torch.Generator`` on the drawing device (the CPU by default, the GPU
+  for the large workloads, where CPU drawing takes minutes) seeded with
+  ``seed`` (0 unless stated), drawn in the fixed order: [sequence lengths],
+  q, k, v, g, beta logits, A_log, dt_bias, [initial_state].  The same seed
+  gives the same values on the same kind of device;
 * the four ``[B,T,H,128]`` tensors are drawn one batch row at a time, so a
   large workload never holds more than one fp32 row in host memory;
 * q, k ~ N(0,1), divided by their L2 norm over the 128 channels of each
@@ -35,7 +37,7 @@ HEAD_DIM = 128
 
 @dataclasses.dataclass
 class KdaInputs:
-    """One workload's inputs on the CPU (move with :meth:`to`)."""
+    """One workload's inputs, on the device they were drawn on (move with :meth:`to`)."""
 
     q: torch.Tensor
     k: torch.Tensor
@@ -68,9 +70,9 @@ class KdaInputs:
 
 
 def _rows(gen, B, T, H, D, unit_rows: bool) -> torch.Tensor:
-    out = torch.empty(B, T, H, D, dtype=torch.bfloat16)
+    out = torch.empty(B, T, H, D, dtype=torch.bfloat16, device=gen.device)
     for b in range(B):
-        x = torch.randn(T, H, D, generator=gen)
+        x = torch.randn(T, H, D, generator=gen, device=gen.device)
         if unit_rows:
             x = x / x.norm(dim=-1, keepdim=True)
         out[b] = x.to(torch.bfloat16)
@@ -84,42 +86,47 @@ def make_inputs(B: int, T: int, H: int, *, lower_bound: float, seed: int = 0,
                 init_dtype: Optional[torch.dtype] = None,
                 final_dtype: Optional[torch.dtype] = None,
                 with_gate_params: bool = True,
-                scale: Optional[float] = None) -> KdaInputs:
+                scale: Optional[float] = None,
+                device: str = "cpu") -> KdaInputs:
     """Draw one workload.
 
     ``varlen=(N, lo, hi)`` draws N lengths in U{lo..hi} (first in the draw
     order) and packs them into one row (B must be 1, T is ignored);
     ``seq_lengths`` packs the given lengths instead.  ``init_dtype`` adds an
     initial state of that dtype; ``final_dtype`` records the dtype the caller
-    wants ``final_state`` in.
+    wants ``final_state`` in.  Tensors are drawn on, and returned on,
+    ``device``; sequence lengths are always drawn on the CPU.
     """
-    gen = torch.Generator().manual_seed(seed)
+    gen = torch.Generator(device=device).manual_seed(seed)
+    cpu_gen = gen if gen.device.type == "cpu" else torch.Generator().manual_seed(seed)
     cu = None
     if varlen is not None or seq_lengths is not None:
         if B != 1:
             raise ValueError("packed sequences need B == 1")
         if varlen is not None:
             n, lo, hi = varlen
-            lens = torch.randint(lo, hi + 1, (n,), generator=gen)
+            lens = torch.randint(lo, hi + 1, (n,), generator=cpu_gen)
             lens = torch.where(lens % 16 == 0, lens - 1, lens)
         else:
             lens = torch.tensor(seq_lengths, dtype=torch.int64)
         cu = torch.zeros(lens.numel() + 1, dtype=torch.int64)
         cu[1:] = torch.cumsum(lens, 0)
         T = int(cu[-1])
+        cu = cu.to(device)
     q = _rows(gen, B, T, H, K, unit_rows=True)
     k = _rows(gen, B, T, H, K, unit_rows=True)
     v = _rows(gen, B, T, H, V, unit_rows=False)
     g = _rows(gen, B, T, H, K, unit_rows=False)
-    beta = torch.randn(B, T, H, generator=gen).to(torch.bfloat16)
+    dev = gen.device
+    beta = torch.randn(B, T, H, generator=gen, device=dev).to(torch.bfloat16)
     A_log = dt_bias = None
     if with_gate_params:
-        A_log = torch.log(torch.rand(H, generator=gen) * 15.0 + 1.0)
-        dt_bias = torch.randn(H, K, generator=gen)
+        A_log = torch.log(torch.rand(H, generator=gen, device=dev) * 15.0 + 1.0)
+        dt_bias = torch.randn(H, K, generator=gen, device=dev)
     init = None
     if init_dtype is not None:
         N = B if cu is None else cu.numel() - 1
-        init = (0.1 * torch.randn(N, H, V, K, generator=gen)).to(init_dtype)
+        init = (0.1 * torch.randn(N, H, V, K, generator=gen, device=dev)).to(init_dtype)
     return KdaInputs(q=q, k=k, v=v, g=g, beta=beta, A_log=A_log, dt_bias=dt_bias,
                      scale=(1.0 / math.sqrt(K)) if scale is None else scale,
                      lower_bound=lower_bound, initial_state=init, cu_seqlens=cu,
@@ -139,6 +146,6 @@ WORKLOADS = {
 }
 
 
-def workload(name: str, seed: int = 0) -> KdaInputs:
-    """Draw one of the five named workloads."""
-    return make_inputs(**WORKLOADS[name], seed=seed)
+def workload(name: str, seed: int = 0, device: str = "cpu") -> KdaInputs:
+    """Draw one of the five named workloads on ``device``."""
+    return make_inputs(**WORKLOADS[name], seed=seed, device=device)

@@ -1,0 +1,125 @@
+/*
+ * kda.h - C ABI of the MI355X (gfx950) Kimi Delta Attention forward library.
+ *
+ * One call, kda_fwd(), runs the chunked KDA forward pass on the GPU: the
+ * per-channel gated delta-rule recurrence over head dimension K = V = 128.
+ * Per (sequence, head) chain and token t (state S is K x V, fp32):
+ *
+ *   a_t  = lower_bound * sigmoid(exp(A_log[h]) * (g_t + dt_bias[h,:]))
+ *   S    = diag(exp(a_t)) S
+ *   S    = S + sigmoid(beta_t) k_t (v_t - S^T k_t)^T
+ *   o_t  = scale * S^T q_t
+ *
+ * Where each piece is defined (the FlashKDA pages):
+ *   - the tensor contract, dtypes, shapes, contiguity, K = V = 128, the
+ *     sigmoid on beta, the optional recurrent states and packed sequences:
+ *     "FlashKDA Input Tensor Shapes and DTypes", all sections;
+ *   - the gate, lower_bound in [-5, 0] and its log2 rescaling
+ *     gate_scale = lower_bound * log2(e): "FlashKDA lower_bound Parameter",
+ *     "Conversion to the Gate Scale Factor" and the FAQ on dt_bias;
+ *   - the base-2 exponent: "Base-2 Exponent Optimization in FlashKDA",
+ *     "Re-basing the Gate Activation";
+ *   - chunks of 16 tokens and the 16x16 unit-triangular inverse:
+ *     "How FlashKDA's CHUNK Size of 16 Improves Numerical Stability",
+ *     "Efficient 16x16 Matrix Inversion".
+ * The pages never write the delta-rule update or the place of A_log; the
+ * library takes the reading above (A_log multiplies the biased gate inside
+ * the sigmoid; decay, then write with the decayed state, then read).
+ *
+ * Ownership and threading: the caller owns every buffer.  All tensor
+ * pointers are DEVICE pointers to contiguous row-major memory on the current
+ * HIP device.  The library allocates nothing, keeps no state between calls,
+ * never synchronises and is safe to call from several host threads.  The
+ * work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ * and completes asynchronously.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes.  Every argument error is detected on the host, before any
+ * work is enqueued, and leaves every buffer untouched. */
+typedef enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_NULL_POINTER = 1,  /* q, k, v, g, beta or out is NULL while T > 0,
+                                  or a state pointer is given with dtype
+                                  KDA_DTYPE_NONE */
+    KDA_ERR_HEAD_DIM = 2,      /* K != 128 or V != 128 */
+    KDA_ERR_LOWER_BOUND = 3,   /* lower_bound outside [-5, 0], or NaN */
+    KDA_ERR_VARLEN_BATCH = 4,  /* cu_seqlens given with B != 1, or num_seqs < 0 */
+    KDA_ERR_STATE_DTYPE = 5,   /* unknown state dtype, or initial_state and
+                                  final_state both given with different dtypes */
+    KDA_ERR_ALIAS = 6,         /* out or final_state overlaps an input, or
+                                  final_state partly overlaps initial_state */
+    KDA_ERR_SIZE = 7,          /* B < 1, H < 1, T < 0, sizes overflow int64,
+                                  or more than 2^31-1 (sequence, head) chains */
+    KDA_ERR_SCALE = 8,         /* scale is not finite */
+    KDA_ERR_LAUNCH = 9         /* the HIP runtime rejected the launch */
+} kda_status;
+
+/* Element type of initial_state / final_state. */
+typedef enum kda_dtype {
+    KDA_DTYPE_NONE = 0,
+    KDA_DTYPE_BF16 = 1,
+    KDA_DTYPE_FP32 = 2
+} kda_dtype;
+
+/*
+ * kda_fwd - chunked KDA forward pass.
+ *
+ *   q, k, g      bf16 [B,T,H,K]; v bf16 [B,T,H,V]; channel index fastest.
+ *   beta         bf16 [B,T,H], logits (the sigmoid is applied inside).
+ *   scale        finite scalar applied to the read-out, o = scale * S^T q.
+ *   out          bf16 [B,T,H,V], written (round to nearest even).  Rows of
+ *                a packed batch that lie outside every sequence are not
+ *                written.
+ *   A_log        fp32 [H] or NULL (NULL acts as A_log = 0).
+ *   dt_bias      fp32 [H,K] or NULL (NULL acts as 0).
+ *   lower_bound  in [-5, 0]; 0 turns the decay off.
+ *   initial_state  [N,H,V,K] of initial_state_dtype (bf16 or fp32), stored
+ *                transposed: element [n,h,v,k] is S[k][v].  NULL = zero.
+ *   final_state  [N,H,V,K] of final_state_dtype, written with the state
+ *                after the last token of each sequence (bf16: round to
+ *                nearest even).  NULL = not written.  It may be the same
+ *                buffer as initial_state (in-place update) but must not
+ *                partly overlap it.
+ *   cu_seqlens   NULL for batch mode (N = B sequences of length T), or a
+ *                device int64 [num_seqs+1] of sequence start offsets into
+ *                the packed token axis (B must be 1; N = num_seqs).  Its
+ *                contents are not read on the host: they should be
+ *                nondecreasing from 0 to T; the kernels clamp every segment
+ *                to [0, T], so bad contents give wrong results, never an
+ *                out-of-bounds access.
+ *   B, T, H      sizes; T may be 0 (then only final_state is written).
+ *   K, V         head dimensions; must both be 128.
+ *   stream       hipStream_t to enqueue on (NULL = default stream).
+ *
+ * Returns KDA_OK once the work is enqueued, or an error code (nothing
+ * enqueued).  num_seqs is ignored in batch mode.
+ */
+kda_status kda_fwd(const void *q, const void *k, const void *v, const void *g,
+                   const void *beta, double scale, void *out,
+                   const float *A_log, const float *dt_bias, double lower_bound,
+                   const void *initial_state, kda_dtype initial_state_dtype,
+                   void *final_state, kda_dtype final_state_dtype,
+                   const int64_t *cu_seqlens, int64_t num_seqs,
+                   int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+                   void *stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *kda_status_string(kda_status status);
+
+/* ABI version of this header (bumped on any signature change). */
+#define KDA_ABI_VERSION 1
+int kda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -1,0 +1,156 @@
+"""Host-side checks of the C-ABI boundary and the Python binding (no GPU).
+
+The library must load and export every entry point ``include/kda.h``
+declares, and every argument error must be reported before any launch, so
+these calls never reach a kernel (the pointers passed are never read).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import gated_delta_rule_36_amd as kda
+from gated_delta_rule_36_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_expected_entry_points():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", _lib.LIBRARY], capture_output=True,
+                        text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (kda_\w+)", nm))
+    assert set(declared_functions()) <= exported
+    assert lib.kda_abi_version() == _lib.ABI_VERSION
+
+
+def test_library_has_gfx950_code_and_no_oracle():
+    data = open(_lib.LIBRARY, "rb").read()
+    assert b"gfx950" in data
+    assert b"kda_oracle" not in data
+
+
+# --------------------------------------------------------------------------
+# C-ABI argument errors (host checks only; pointers are dummies)
+# --------------------------------------------------------------------------
+
+FAKE = [ctypes.create_string_buffer(64) for _ in range(12)]
+ADDR = [ctypes.addressof(b) for b in FAKE]
+
+
+def call(**over):
+    """kda_fwd with well-formed dummy arguments, some replaced by ``over``."""
+    a = dict(q=ADDR[0], k=ADDR[1], v=ADDR[2], g=ADDR[3], beta=ADDR[4], scale=0.1,
+             out=ADDR[5], A_log=ADDR[6], dt_bias=ADDR[7], lower_bound=-5.0,
+             init=None, init_dtype=0, final=None, final_dtype=0, cu=None, num_seqs=0,
+             B=1, T=0, H=1, K=128, V=128)
+    a.update(over)
+    return _lib.load().kda_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["scale"], a["out"],
+                               a["A_log"], a["dt_bias"], a["lower_bound"], a["init"],
+                               a["init_dtype"], a["final"], a["final_dtype"], a["cu"],
+                               a["num_seqs"], a["B"], a["T"], a["H"], a["K"], a["V"], None)
+
+
+# The dummy buffers are only 64 bytes, but the size checks use the declared
+# shapes; with T = 0 nothing is launched even when every check passes, so the
+# base call must fail only on the planted error.  Overlap checks see the
+# dummies' real addresses with the declared sizes, so calls that would
+# otherwise pass with T > 0 are never made.
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None, T=1), _lib.KDA_ERR_NULL_POINTER),
+    (dict(beta=None, T=1), _lib.KDA_ERR_NULL_POINTER),
+    (dict(out=None, T=1), _lib.KDA_ERR_NULL_POINTER),
+    (dict(init=ADDR[8], init_dtype=0), _lib.KDA_ERR_NULL_POINTER),
+    (dict(K=64), _lib.KDA_ERR_HEAD_DIM),
+    (dict(V=256), _lib.KDA_ERR_HEAD_DIM),
+    (dict(lower_bound=0.5), _lib.KDA_ERR_LOWER_BOUND),
+    (dict(lower_bound=-5.0001), _lib.KDA_ERR_LOWER_BOUND),
+    (dict(lower_bound=math.nan), _lib.KDA_ERR_LOWER_BOUND),
+    (dict(cu=ADDR[9], num_seqs=1, B=2), _lib.KDA_ERR_VARLEN_BATCH),
+    (dict(cu=ADDR[9], num_seqs=-1), _lib.KDA_ERR_VARLEN_BATCH),
+    (dict(init=ADDR[8], init_dtype=1, final=ADDR[10], final_dtype=2), _lib.KDA_ERR_STATE_DTYPE),
+    (dict(init=ADDR[8], init_dtype=7), _lib.KDA_ERR_STATE_DTYPE),
+    (dict(out=ADDR[0], T=1), _lib.KDA_ERR_ALIAS),
+    (dict(final=ADDR[3], final_dtype=2, T=1), _lib.KDA_ERR_ALIAS),
+    (dict(init=ADDR[8], init_dtype=2, final=ADDR[8] + 4, final_dtype=2), _lib.KDA_ERR_ALIAS),
+    (dict(B=0), _lib.KDA_ERR_SIZE),
+    (dict(H=0), _lib.KDA_ERR_SIZE),
+    (dict(T=-1), _lib.KDA_ERR_SIZE),
+    (dict(B=1 << 40, T=1 << 30), _lib.KDA_ERR_SIZE),
+    (dict(scale=math.inf), _lib.KDA_ERR_SCALE),
+    (dict(scale=math.nan), _lib.KDA_ERR_SCALE),
+])
+def test_argument_errors_are_reported_before_launch(over, code):
+    assert call(**over) == code
+
+
+def test_status_strings_are_distinct():
+    msgs = [_lib.status_string(c) for c in range(10)]
+    assert len(set(msgs)) == 10 and msgs[0] == "ok"
+    assert _lib.status_string(123) == "unknown status"
+
+
+def test_empty_token_tensors_may_be_null():
+    """With T = 0 the token tensors are empty (torch gives them a NULL data
+    pointer), which is accepted; packed mode with no sequence launches
+    nothing, so this stays a host-only call."""
+    assert call(q=None, k=None, v=None, g=None, beta=None, out=None, cu=ADDR[9],
+                num_seqs=0) == _lib.KDA_OK
+
+
+def test_zero_sequences_is_a_no_op():
+    # packed mode with N = 0 has no chain: OK without a launch
+    assert call(cu=ADDR[9], num_seqs=0) == _lib.KDA_OK
+
+
+# --------------------------------------------------------------------------
+# Python binding checks (raised before the library is called)
+# --------------------------------------------------------------------------
+
+def _cpu_args(**over):
+    B, T, H = 1, 4, 2
+    a = dict(q=torch.zeros(B, T, H, 128, dtype=torch.bfloat16),
+             k=torch.zeros(B, T, H, 128, dtype=torch.bfloat16),
+             v=torch.zeros(B, T, H, 128, dtype=torch.bfloat16),
+             g=torch.zeros(B, T, H, 128, dtype=torch.bfloat16),
+             beta=torch.zeros(B, T, H, dtype=torch.bfloat16), scale=0.1,
+             out=torch.zeros(B, T, H, 128, dtype=torch.bfloat16),
+             A_log=torch.zeros(H), dt_bias=torch.zeros(H, 128), lower_bound=-5.0)
+    a.update(over)
+    return a
+
+
+def test_binding_rejects_wrong_dtype():
+    with pytest.raises(TypeError):
+        kda.fwd(**_cpu_args(q=torch.zeros(1, 4, 2, 128)))
+    with pytest.raises(TypeError):
+        kda.fwd(**_cpu_args(beta=torch.zeros(1, 4, 2)))
+
+
+def test_binding_rejects_host_tensors():
+    with pytest.raises(ValueError, match="GPU"):
+        kda.fwd(**_cpu_args())
+
+
+def test_binding_rejects_non_tensors():
+    with pytest.raises(TypeError):
+        kda.fwd(**_cpu_args(q=[1, 2, 3]))
