@@ -5,6 +5,8 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
+#include <cstring>
 
 #include "kda_internal.h"
 
@@ -49,7 +51,7 @@ extern "C" kda_status kda_fwd(const void *q, const void *k, const void *v, const
         return KDA_ERR_LOWER_BOUND;
     if (!std::isfinite(scale))
         return KDA_ERR_SCALE;
-    if (B < 1 || H < 1 || T < 0)
+    if (B < 1 || H < 1 || T < 0 || T > INT32_MAX)
         return KDA_ERR_SIZE;
     if (cu_seqlens && (B != 1 || num_seqs < 0))
         return KDA_ERR_VARLEN_BATCH;
@@ -141,8 +143,14 @@ extern "C" const char *kda_status_string(kda_status status)
 extern "C" int kda_abi_version(void) { return KDA_ABI_VERSION; }
 
 namespace kda {
+// The MFMA kernel is the forward pass.  KDA_KERNEL=simt selects the plain
+// fp32 kernel instead (same results within rounding; for cross-checks).
 hipError_t launch_forward(const FwdParams &p, hipStream_t stream)
 {
-    return launch_chunk_simt(p, stream);
+    static const bool use_simt = [] {
+        const char *e = std::getenv("KDA_KERNEL");
+        return e && std::strcmp(e, "simt") == 0;
+    }();
+    return use_simt ? launch_chunk_simt(p, stream) : launch_chunk_mfma(p, stream);
 }
 }  // namespace kda

@@ -1,0 +1,585 @@
+// Chunked KDA forward kernel for gfx950: bf16 MFMA for every contraction,
+// fp32 state held in accumulator registers, one workgroup of 8 waves per
+// (sequence, head) chain.
+//
+// The chunk-of-16 form (gate a in log2 units, G = inclusive sum of a over
+// the chunk, Gamma = 2^G, Gamma_C = its value at the chunk's last token):
+//   Qt = scale q Gamma, Kt = k Gamma, Kbar = k Gamma_C / Gamma, Kh = Kbar / Gamma_C
+//   A  = diag(beta) Kt Kh^T (strictly lower),  P = Qt Kh^T (lower)
+//   T  = (I + A)^-1,  W = T diag(beta) Kt,  U~ = T diag(beta) V
+//   U  = U~ - W S,  O = Qt S + P U,  S <- diag(Gamma_C) S + Kbar^T U
+// The 16-token chunk keeps 2^(+-G) within the bf16/fp32 exponent range for
+// lower_bound >= -5 (chunk-size page, "bf16 Dynamic Range and Exponential
+// Terms"); the unit lower-triangular 16x16 inverse is the one the same page
+// describes under "Efficient 16x16 Matrix Inversion" (solved here by forward
+// substitution in fp32).
+//
+// Wave roles (64-lane waves; lane = 16 * g4 + l16):
+//   waves 0-3  "state" waves.  Wave w owns the 128 x 32 slab S[:, 32w:32w+32]
+//              of the state as 16 fp32 16x16 accumulator tiles and, per chunk,
+//              computes U = U~ - W S, O = Qt S + P U (stores out) and the
+//              state update.  S is the B operand of W S and Qt S through a
+//              fixed permutation of the contraction index, so the fp32
+//              accumulators convert to bf16 operands in place.
+//   waves 4-7  "chunk" waves.  Wave p owns channels (and value columns)
+//              32p..32p+31 and runs, for three different chunks at once:
+//                G   stream in q/k/g/v (16-byte loads issued three chunks
+//                    ahead), transpose to channel-major with an MFMA against
+//                    a 0/1 selection matrix, gate, cumulative decay products,
+//                    the decayed operands (written to LDS in the layouts the
+//                    MFMAs read);
+//                SOL A = diag(beta) Kt Kh^T, then four columns of T by
+//                    forward substitution (and, wave 4 only, P);
+//                WY  W and U~ for its 32 columns from T diag(beta) (split in
+//                    two bf16 halves for precision).
+// Iteration `it` runs G(it), SOL(it-1), WY(it-2) and the state update of
+// chunk it-3; a single workgroup barrier per iteration orders every hand-off
+// through LDS.
+#include <hip/hip_runtime.h>
+
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int C = kChunk;
+constexpr int D = kHeadDim;
+constexpr int kThreads = 512;
+constexpr int kRawSets = 4;  // raw chunks in registers: the current one + 3 in flight
+
+struct __align__(16) Shared {
+    uint16_t kt_row[2][C][D];  // Kt, token-major (bf16)
+    uint16_t kh_row[2][C][D];  // Kh, token-major
+    uint16_t qt_row[4][C][D];  // Qt (scale folded in), token-major
+    uint16_t kt_col[3][D][C];  // Kt, channel-major
+    uint16_t v_col[3][D][C];   // V, column-major
+    uint16_t kb_col[4][D][C];  // Kbar, channel-major
+    float gam_c[4][D];         // Gamma_C per channel
+    float beta[2][C];          // sigmoid(beta logits), 0 on padding rows
+    float amat[4][C][C];       // A, one private copy per chunk wave
+    uint16_t tb_hi[2][C][C];   // T diag(beta) = hi + lo, two bf16 parts
+    uint16_t tb_lo[2][C][C];
+    uint16_t pmat[3][C][C];    // P
+    uint16_t w_row[2][C][D];   // W, token-major
+    float ut[2][D][C];         // U~, column-major
+    uint16_t ostage[4][C][32]; // output transpose, one per state wave
+};
+
+struct RawChunk {
+    u32x4_t q, k, g, v;  // 8 bf16 each: one token, 8 consecutive channels
+    uint32_t beta;       // bf16 logit in the low half (wave 4, lanes 0-15)
+};
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
+{
+    bf16x2_t v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+    return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ u32x2_t pack_bf16x4(f32x4_t x)
+{
+    return u32x2_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+}
+__device__ __forceinline__ f32x4_t mfma32(bf16x8_t a, bf16x8_t b, f32x4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma16(u32x2_t a, u32x2_t b, f32x4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
+                                                     __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8_t cat8(u32x2_t lo, u32x2_t hi)
+{
+    return __builtin_bit_cast(bf16x8_t, u32x4_t{lo[0], lo[1], hi[0], hi[1]});
+}
+template <typename V>
+__device__ __forceinline__ V lds_load(const void *p)
+{
+    return *static_cast<const V *>(p);
+}
+template <typename V>
+__device__ __forceinline__ void lds_store(void *p, V v)
+{
+    *static_cast<V *>(p) = v;
+}
+
+// Workgroup barrier that orders LDS only.  Outstanding global loads (the
+// prefetch) stay in flight across it.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Broadcast lane `m` of each 16-lane row to the whole row.
+template <int M>
+__device__ __forceinline__ float row_bcast(float x)
+{
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + M, 0xF, 0xF, false));
+}
+
+// ---------------------------------------------------------------------------
+// chunk waves
+// ---------------------------------------------------------------------------
+
+struct ChunkWave {
+    const FwdParams &p;
+    Shared &sh;
+    int64_t t_begin, t_end;
+    int nchunks;
+    int pw;  // 0..3
+    int lane, l16, g4;
+    const uint16_t *src_q, *src_k, *src_g, *src_v;  // this lane's 8 channels at token t_begin
+    const uint16_t *src_beta;                       // beta at token t_begin
+    int64_t tok_stride;                             // elements between tokens (H * 128)
+    int64_t beta_stride;                            // H
+    float head_neg;     // -exp(A_log[h]) * log2(e)
+    float bias_neg[2];  // head_neg * dt_bias[h][ch] for the two 16-channel tiles
+    bf16x8_t sel[2];    // 0/1 selection matrices for the channel-major transposes
+    u32x2_t ident;      // 16x16 identity as an x16 B operand
+
+    __device__ int chunk_len(int x) const
+    {
+        const int64_t left = t_end - (t_begin + int64_t(x) * C);
+        return static_cast<int>(left < C ? left : C);
+    }
+
+    // Loads are unconditional: a row past the sequence end re-reads the
+    // chunk's first token (always inside the tensors) and is masked later.
+    __device__ void load(int x, RawChunk &r) const
+    {
+        const int len = chunk_len(x);
+        const int64_t tok = int64_t(x) * C + (l16 < len ? l16 : 0);
+        const int64_t btok = int64_t(x) * C + (lane < len ? lane : 0);
+        r.beta = src_beta[btok * beta_stride];
+        const int64_t e = tok * tok_stride;
+        r.q = *reinterpret_cast<const u32x4_t *>(src_q + e);
+        r.k = *reinterpret_cast<const u32x4_t *>(src_k + e);
+        r.g = *reinterpret_cast<const u32x4_t *>(src_g + e);
+        r.v = *reinterpret_cast<const u32x4_t *>(src_v + e);
+    }
+
+    // G: gate, decay products and the decayed operands of chunk x.
+    __device__ void gate_stage(int x, int s3, const RawChunk &r) const
+    {
+        const int len = chunk_len(x);
+        const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+        const int s2 = x & 1, s4 = x & 3;
+        {
+            const float b = sigmoid_f32(bf16_to_f32(static_cast<uint16_t>(r.beta)));
+            if (pw == 0 && lane < C)
+                sh.beta[s2][lane] = lane < len ? b : 0.f;
+        }
+
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            // channel-major tiles: lane (l16, g4) holds tokens 4*g4 + i of
+            // channel 32*pw + 16*t + l16
+            f32x4_t cq = mfma32(__builtin_bit_cast(bf16x8_t, r.q), sel[t], zero);
+            f32x4_t ck = mfma32(__builtin_bit_cast(bf16x8_t, r.k), sel[t], zero);
+            const f32x4_t cg = mfma32(__builtin_bit_cast(bf16x8_t, r.g), sel[t], zero);
+            f32x4_t cv = mfma32(__builtin_bit_cast(bf16x8_t, r.v), sel[t], zero);
+
+            // rows past the sequence end: no write (k = v = 0), no read-out
+            // (q = 0) and no decay (alpha = 1)
+            float al[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool valid = 4 * g4 + i < len;
+                const float e = exp2_f32(fmaf(cg[i], head_neg, bias_neg[t]));
+                const float s = __builtin_amdgcn_rcpf(1.0f + e);
+                const float a = exp2_f32(p.gate_scale * s);
+                al[i] = valid ? a : 1.0f;
+                cq[i] = valid ? cq[i] : 0.0f;
+                ck[i] = valid ? ck[i] : 0.0f;
+                cv[i] = valid ? cv[i] : 0.0f;
+            }
+            // products within the 4-token group, then across the 4 groups
+            const float p0 = al[0], p1 = p0 * al[1], p2 = p1 * al[2], p3 = p2 * al[3];
+            const float s3_ = 1.0f, s2_ = al[3], s1_ = al[2] * al[3], s0_ = al[1] * s1_;
+            const float P0 = __shfl(p3, l16), P1 = __shfl(p3, l16 + 16),
+                        P2 = __shfl(p3, l16 + 32), P3 = __shfl(p3, l16 + 48);
+            const float P01 = P0 * P1, P012 = P01 * P2, gc = P012 * P3;
+            const float P23 = P2 * P3, P123 = P1 * P23;
+            const float pre = g4 == 0 ? 1.0f : (g4 == 1 ? P0 : (g4 == 2 ? P01 : P012));
+            const float suf = g4 == 3 ? 1.0f : (g4 == 2 ? P3 : (g4 == 1 ? P23 : P123));
+            const float inv_gc = __builtin_amdgcn_rcpf(gc);
+            const float gam[4] = {pre * p0, pre * p1, pre * p2, pre * p3};
+            const float gbar[4] = {s0_ * suf, s1_ * suf, s2_ * suf, s3_ * suf};
+
+            f32x4_t kt, qt, kb, kh;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                kt[i] = ck[i] * gam[i];
+                qt[i] = cq[i] * (p.scale * gam[i]);
+                kb[i] = ck[i] * gbar[i];
+                kh[i] = kb[i] * inv_gc;
+            }
+            const int ch = 32 * pw + 16 * t + l16;
+            const u32x2_t kt2 = pack_bf16x4(kt), qt2 = pack_bf16x4(qt), kb2 = pack_bf16x4(kb),
+                          kh2 = pack_bf16x4(kh), v2 = pack_bf16x4(cv);
+            lds_store(&sh.kt_col[s3][ch][4 * g4], kt2);
+            lds_store(&sh.v_col[s3][ch][4 * g4], v2);
+            lds_store(&sh.kb_col[s4][ch][4 * g4], kb2);
+            if (g4 == 0)
+                sh.gam_c[s4][ch] = gc;
+            // token-major copies: (X^T I) puts 4 consecutive channels of one
+            // token in each lane
+            const int col = 32 * pw + 16 * t + 4 * g4;
+            lds_store(&sh.kt_row[s2][l16][col], pack_bf16x4(mfma16(kt2, ident, zero)));
+            lds_store(&sh.kh_row[s2][l16][col], pack_bf16x4(mfma16(kh2, ident, zero)));
+            lds_store(&sh.qt_row[s4][l16][col], pack_bf16x4(mfma16(qt2, ident, zero)));
+        }
+    }
+
+    // SOL: A, four columns of T, and (wave 4) P for chunk x.
+    __device__ void solve_stage(int x, int s3) const
+    {
+        const int s2 = x & 1, s4 = x & 3;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, pacc = acc;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            const int col = 32 * kt + 8 * g4;
+            const bf16x8_t a = lds_load<bf16x8_t>(&sh.kt_row[s2][l16][col]);
+            const bf16x8_t b = lds_load<bf16x8_t>(&sh.kh_row[s2][l16][col]);
+            acc = mfma32(a, b, acc);
+            if (pw == 0) {
+                const bf16x8_t q = lds_load<bf16x8_t>(&sh.qt_row[s4][l16][col]);
+                pacc = mfma32(b, q, pacc);
+            }
+        }
+        // acc: lane (j = l16, g4) holds (Kt Kh^T)[4*g4 + i][j]
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row_i = 4 * g4 + i;
+            sh.amat[pw][row_i][l16] = l16 < row_i ? sh.beta[s2][row_i] * acc[i] : 0.f;
+        }
+        if (pw == 0) {
+            // pacc: lane (i = l16, g4) holds P[i][4*g4 + e]
+            f32x4_t pm;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pm[e] = (4 * g4 + e <= l16) ? pacc[e] : 0.f;
+            lds_store(&sh.pmat[s3][l16][4 * g4], pack_bf16x4(pm));
+        }
+
+        // T[:, j] for j = 4*pw + g4; lane (g4, l16 = row i).  Right-looking
+        // forward substitution: once t_m is known, every later row adds
+        // A[i][m] t_m to its running sum.
+        const int j = 4 * pw + g4, i = l16;
+        float arow[C];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4_t v = lds_load<f32x4_t>(&sh.amat[pw][i][4 * q4]);
+            arow[4 * q4 + 0] = v[0];
+            arow[4 * q4 + 1] = v[1];
+            arow[4 * q4 + 2] = v[2];
+            arow[4 * q4 + 3] = v[3];
+        }
+        float run = 0.f, t_i = 0.f;
+        solve_steps(arow, j, i, run, t_i);
+        const float tb = t_i * sh.beta[s2][j];
+        const __bf16 hi = static_cast<__bf16>(tb);
+        const __bf16 lo = static_cast<__bf16>(tb - static_cast<float>(hi));
+        sh.tb_hi[s2][i][j] = __builtin_bit_cast(uint16_t, hi);
+        sh.tb_lo[s2][i][j] = __builtin_bit_cast(uint16_t, lo);
+    }
+
+    template <int M = 0>
+    __device__ __forceinline__ void solve_steps(const float (&arow)[C], int j, int i, float &run,
+                                                float &t_i) const
+    {
+        if constexpr (M < C) {
+            const float own = (M == j) ? 1.0f : (M > j ? -run : 0.0f);
+            const float tm = row_bcast<M>(own);
+            if (i == M)
+                t_i = tm;
+            if (i > M)
+                run = fmaf(arow[M], tm, run);
+            solve_steps<M + 1>(arow, j, i, run, t_i);
+        }
+    }
+
+    // WY: W and U~ for this wave's 32 columns of chunk x.
+    __device__ void wy_stage(int x, int s3) const
+    {
+        const int s2 = x & 1;
+        const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+        // lane (l16, g4) holds (T diag(beta))[l16][4*g4 .. 4*g4+3]: the A operand
+        // of T diag(beta) V and the B operand of Kt^T (T diag(beta))^T
+        const u32x2_t th = lds_load<u32x2_t>(&sh.tb_hi[s2][l16][4 * g4]);
+        const u32x2_t tl = lds_load<u32x2_t>(&sh.tb_lo[s2][l16][4 * g4]);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int ch = 32 * pw + 16 * t + l16;
+            const u32x2_t ka = lds_load<u32x2_t>(&sh.kt_col[s3][ch][4 * g4]);
+            f32x4_t w = mfma16(ka, th, zero);
+            w = mfma16(ka, tl, w);  // lane (token l16, g4): W[l16][32pw+16t+4g4+i]
+            lds_store(&sh.w_row[s2][l16][32 * pw + 16 * t + 4 * g4], pack_bf16x4(w));
+            const u32x2_t vb = lds_load<u32x2_t>(&sh.v_col[s3][ch][4 * g4]);
+            f32x4_t u = mfma16(th, vb, zero);
+            u = mfma16(tl, vb, u);  // lane (vcol, g4): U~[4g4+i][vcol]
+            lds_store(&sh.ut[s2][ch][4 * g4], u);
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// state waves
+// ---------------------------------------------------------------------------
+
+template <int INIT, int FINAL>
+struct StateWave {
+    const FwdParams &p;
+    Shared &sh;
+    int64_t t_begin, t_end, chain;
+    int w, lane, l16, g4;
+    uint16_t *dst_out;   // out at token t_begin, this lane's 8 value columns
+    int64_t tok_stride;  // H * 128
+    f32x4_t S[8][2];     // S[16mt + 4g4 + i][32w + 16nt + l16]
+
+    __device__ int64_t state_index(int mt, int nt) const
+    {
+        return (chain * D + 32 * w + 16 * nt + l16) * D + 16 * mt + 4 * g4;
+    }
+
+    __device__ void load_state()
+    {
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const int64_t idx = state_index(mt, nt);
+                if constexpr (INIT == kStateFp32) {
+                    S[mt][nt] = *reinterpret_cast<const f32x4_t *>(
+                        static_cast<const float *>(p.init_state) + idx);
+                } else if constexpr (INIT == kStateBf16) {
+                    const u32x2_t b = *reinterpret_cast<const u32x2_t *>(
+                        static_cast<const uint16_t *>(p.init_state) + idx);
+                    S[mt][nt] = f32x4_t{__uint_as_float(b[0] << 16), __uint_as_float(b[0] & 0xffff0000u),
+                                        __uint_as_float(b[1] << 16), __uint_as_float(b[1] & 0xffff0000u)};
+                } else {
+                    S[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+    }
+
+    __device__ void store_state() const
+    {
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const int64_t idx = state_index(mt, nt);
+                if constexpr (FINAL == kStateFp32) {
+                    *reinterpret_cast<f32x4_t *>(static_cast<float *>(p.final_state) + idx) = S[mt][nt];
+                } else if constexpr (FINAL == kStateBf16) {
+                    *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(p.final_state) + idx) =
+                        u32x2_t{uint32_t(f32_to_bf16_rne(S[mt][nt][0])) |
+                                    (uint32_t(f32_to_bf16_rne(S[mt][nt][1])) << 16),
+                                uint32_t(f32_to_bf16_rne(S[mt][nt][2])) |
+                                    (uint32_t(f32_to_bf16_rne(S[mt][nt][3])) << 16)};
+                }
+            }
+    }
+
+    __device__ void chunk(int x, int s3)
+    {
+        const int s2 = x & 1, s4 = x & 3;
+        const int64_t left = t_end - (t_begin + int64_t(x) * C);
+        const int len = static_cast<int>(left < C ? left : C);
+
+        // S as bf16 B operands; contraction slot 8*g4 + e maps to state row
+        // 32kt + 4g4 + e (e < 4) and 32kt + 16 + 4g4 + (e - 4) (e >= 4), which
+        // is exactly what this lane's accumulators of tiles 2kt, 2kt+1 hold.
+        bf16x8_t sb[4][2];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+                sb[kt][nt] = cat8(pack_bf16x4(S[2 * kt][nt]), pack_bf16x4(S[2 * kt + 1][nt]));
+
+        f32x4_t X[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        f32x4_t Y[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            const bf16x8_t wa = cat8(lds_load<u32x2_t>(&sh.w_row[s2][l16][32 * kt + 4 * g4]),
+                                     lds_load<u32x2_t>(&sh.w_row[s2][l16][32 * kt + 16 + 4 * g4]));
+            const bf16x8_t qa = cat8(lds_load<u32x2_t>(&sh.qt_row[s4][l16][32 * kt + 4 * g4]),
+                                     lds_load<u32x2_t>(&sh.qt_row[s4][l16][32 * kt + 16 + 4 * g4]));
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                X[nt] = mfma32(wa, sb[kt][nt], X[nt]);
+                Y[nt] = mfma32(qa, sb[kt][nt], Y[nt]);
+            }
+        }
+
+        // U = U~ - W S, as bf16 B operands (lane (vcol, g4): tokens 4g4..4g4+3)
+        u32x2_t ub[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const f32x4_t u = lds_load<f32x4_t>(&sh.ut[s2][32 * w + 16 * nt + l16][4 * g4]) - X[nt];
+            ub[nt] = pack_bf16x4(u);
+        }
+
+        // O = Qt S + P U, staged through LDS for 16-byte row stores
+        const u32x2_t pa = lds_load<u32x2_t>(&sh.pmat[s3][l16][4 * g4]);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const f32x4_t o = mfma16(pa, ub[nt], Y[nt]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                sh.ostage[w][4 * g4 + i][16 * nt + l16] = f32_to_bf16_rne(o[i]);
+        }
+        {
+            const int tk = lane >> 2, sg = lane & 3;
+            const u32x4_t ov = lds_load<u32x4_t>(&sh.ostage[w][tk][8 * sg]);
+            if (tk < len)
+                *reinterpret_cast<u32x4_t *>(dst_out + (int64_t(x) * C + tk) * tok_stride) = ov;
+        }
+
+        // S <- diag(Gamma_C) S + Kbar^T U
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            const f32x4_t gc = lds_load<f32x4_t>(&sh.gam_c[s4][16 * mt + 4 * g4]);
+            const u32x2_t ka = lds_load<u32x2_t>(&sh.kb_col[s4][16 * mt + l16][4 * g4]);
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) S[mt][nt] = mfma16(ka, ub[nt], S[mt][nt] * gc);
+        }
+    }
+};
+
+template <int INIT, int FINAL>
+__global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
+{
+    __shared__ Shared sh;
+    const int64_t chain = blockIdx.x;
+    const int64_t n = chain / p.H, h = chain % p.H;
+    int64_t t_begin, t_end, row;
+    chain_segment(p, n, &t_begin, &t_end, &row);
+    const int64_t nchunks = (t_end - t_begin + C - 1) / C;  // < 2^31 (T is bounded on the host)
+    const int n_iter = nchunks > 0 ? static_cast<int>(nchunks) + 3 : 0;
+
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int64_t tok_stride = p.H * D;
+    const int64_t first = (row * p.T + t_begin) * p.H + h;  // token-head row of t_begin
+
+    if (wave < 4) {
+        StateWave<INIT, FINAL> sw{p, sh, t_begin, t_end, chain, wave, lane, l16, g4,
+                                  p.out + first * D + 32 * wave + 8 * (lane & 3), tok_stride, {}};
+        sw.load_state();
+        int s3 = 0;  // chunk index mod 3 of the chunk being updated
+        for (int it = 0; it < n_iter; ++it) {
+            if (it >= 3) {
+                sw.chunk(it - 3, s3);
+                s3 = s3 == 2 ? 0 : s3 + 1;
+            }
+            lds_barrier();
+        }
+        sw.store_state();
+        return;
+    }
+
+    const int pw = wave - 4;
+    const int64_t lane_off = first * D + 32 * pw + 8 * g4;
+    ChunkWave cw{p, sh, t_begin, t_end, static_cast<int>(nchunks), pw, lane, l16, g4,
+                 p.q + lane_off, p.k + lane_off, p.g + lane_off, p.v + lane_off,
+                 p.beta + first, tok_stride, p.H};
+    const float head_mult = p.A_log ? expf(p.A_log[h]) : 1.0f;
+    cw.head_neg = -head_mult * kLog2eF;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int ch = 32 * pw + 16 * t + l16;
+        cw.bias_neg[t] = p.dt_bias ? cw.head_neg * p.dt_bias[h * D + ch] : 0.f;
+        // selection matrix: element e of lane (l16, g4) is 1 when contraction
+        // index 8*g4 + e equals channel 16*t + l16
+        bf16x8_t sel;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sel[e] = static_cast<__bf16>((8 * g4 + e == 16 * t + l16) ? 1.0f : 0.0f);
+        cw.sel[t] = sel;
+    }
+    {
+        uint16_t idb[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) idb[e] = (4 * g4 + e == l16) ? 0x3F80 : 0;
+        cw.ident = u32x2_t{uint32_t(idb[0]) | (uint32_t(idb[1]) << 16),
+                           uint32_t(idb[2]) | (uint32_t(idb[3]) << 16)};
+    }
+    if (n_iter == 0)
+        return;
+
+    const int nc = static_cast<int>(nchunks);
+    RawChunk raw[kRawSets];
+#pragma unroll
+    for (int s = 0; s < kRawSets - 1; ++s) cw.load(s < nc ? s : nc - 1, raw[s]);
+
+    // mod-3 slots of the chunks handled by G, SOL and WY in this iteration
+    int g3 = 0, sol3 = 2, wy3 = 1;
+    // G runs in every iteration: past the last chunk it only fills LDS slots
+    // that no later stage reads, which keeps the prefetch bookkeeping simple.
+    auto step = [&](int it, RawChunk &cur, RawChunk &next) {
+        cw.gate_stage(it, g3, cur);
+        {
+            const int ahead = it + kRawSets - 1;
+            cw.load(ahead < nc ? ahead : nc - 1, next);
+        }
+        if (it >= 1 && it - 1 < nc)
+            cw.solve_stage(it - 1, sol3);
+        if (it >= 2 && it - 2 < nc)
+            cw.wy_stage(it - 2, wy3);
+        g3 = g3 == 2 ? 0 : g3 + 1;
+        sol3 = sol3 == 2 ? 0 : sol3 + 1;
+        wy3 = wy3 == 2 ? 0 : wy3 + 1;
+        lds_barrier();
+    };
+    for (int it0 = 0; it0 < n_iter; it0 += kRawSets) {
+        step(it0, raw[0], raw[3]);
+        if (it0 + 1 >= n_iter) break;
+        step(it0 + 1, raw[1], raw[0]);
+        if (it0 + 2 >= n_iter) break;
+        step(it0 + 2, raw[2], raw[1]);
+        if (it0 + 3 >= n_iter) break;
+        step(it0 + 3, raw[3], raw[2]);
+    }
+}
+
+template <int INIT, int FINAL>
+hipError_t launch(const FwdParams &p, hipStream_t stream)
+{
+    const int64_t chains = p.num_seqs * p.H;
+    FwdParams args = p;
+    void *argv[] = {&args};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&chunk_mfma_kernel<INIT, FINAL>),
+                           dim3(static_cast<unsigned>(chains)), dim3(kThreads), argv, 0, stream);
+}
+
+template <int INIT>
+hipError_t launch_final(const FwdParams &p, hipStream_t stream)
+{
+    switch (p.final_kind) {
+    case kStateBf16: return launch<INIT, kStateBf16>(p, stream);
+    case kStateFp32: return launch<INIT, kStateFp32>(p, stream);
+    default: return launch<INIT, kStateNone>(p, stream);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_chunk_mfma(const FwdParams &p, hipStream_t stream)
+{
+    switch (p.init_kind) {
+    case kStateBf16: return launch_final<kStateBf16>(p, stream);
+    case kStateFp32: return launch_final<kStateFp32>(p, stream);
+    default: return launch_final<kStateNone>(p, stream);
+    }
+}
+
+}  // namespace kda

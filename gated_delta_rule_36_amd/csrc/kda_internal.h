@@ -33,6 +33,7 @@ struct FwdParams {
 hipError_t launch_forward(const FwdParams &p, hipStream_t stream);
 
 // Individual kernel launchers (one per implementation).
+hipError_t launch_chunk_mfma(const FwdParams &p, hipStream_t stream);
 hipError_t launch_chunk_simt(const FwdParams &p, hipStream_t stream);
 
 }  // namespace kda
