@@ -53,24 +53,43 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int C = kChunk;
 constexpr int D = kHeadDim;
 constexpr int kThreads = 512;
-constexpr int kRawSets = 4;  // raw chunks in registers: the current one + 3 in flight
+constexpr int kRawSlots = 3;  // chunks staged in LDS: the one being read + 2 in flight
+
+// LDS bank layout (64 banks of 4 bytes): every access below is arranged so
+// that the lanes served together hit distinct banks.
+//  * Token-major tiles are read and written one token row per lane; their
+//    rows are padded by 16 bytes so the 16 rows fall in different banks.
+//  * 16-element rows (channel-major bf16 tiles, 32 bytes) are accessed in
+//    4-element chunks by lane (row l16, chunk g4); rows r and r + 8 share
+//    banks, so chunk g is stored at g ^ (2 * bit 3 of r).
+//  * 16-element fp32 rows (64 bytes) are accessed in 4-element chunks by
+//    16 lanes at a time; rows r, r+4, r+8, r+12 share banks, so chunk g is
+//    stored at g ^ (bits 2-3 of r).
+constexpr int DP = D + 8;
+constexpr int AP = C + 4;  // padded row of the fp32 A matrix
+
+__device__ __forceinline__ int chunk16(int r, int g) { return 4 * (g ^ (((r >> 3) & 1) << 1)); }
+__device__ __forceinline__ int chunk32(int r, int g) { return 4 * (g ^ ((r >> 2) & 3)); }
 
 struct __align__(16) Shared {
-    uint16_t kt_row[2][C][D];  // Kt, token-major (bf16)
-    uint16_t kh_row[2][C][D];  // Kh, token-major
-    uint16_t qt_row[4][C][D];  // Qt (scale folded in), token-major
+    uint16_t kt_row[2][C][DP];  // Kt, token-major (bf16)
+    uint16_t kh_row[2][C][DP];  // Kh, token-major
+    uint16_t qt_row[4][C][DP];  // Qt (scale folded in), token-major
     uint16_t kt_col[3][D][C];  // Kt, channel-major
     uint16_t v_col[3][D][C];   // V, column-major
     uint16_t kb_col[4][D][C];  // Kbar, channel-major
     float gam_c[4][D];         // Gamma_C per channel
     float beta[2][C];          // sigmoid(beta logits), 0 on padding rows
-    float amat[4][C][C];       // A, one private copy per chunk wave
+    float amat[C][AP];         // A; every chunk wave writes the same values
     uint16_t tb_hi[2][C][C];   // T diag(beta) = hi + lo, two bf16 parts
     uint16_t tb_lo[2][C][C];
     uint16_t pmat[3][C][C];    // P
-    uint16_t w_row[2][C][D];   // W, token-major
+    uint16_t w_row[2][C][DP];  // W, token-major
     float ut[2][D][C];         // U~, column-major
-    uint16_t ostage[4][C][32]; // output transpose, one per state wave
+    // raw q, k, g, v of a chunk as fetched by each chunk wave (16 bytes per
+    // lane, lane order), and the beta logits (zero-extended, chunk wave 0)
+    u32x4_t raw[kRawSlots][4][4][64];
+    uint32_t raw_beta[kRawSlots][64];
 };
 
 struct RawChunk {
@@ -118,6 +137,34 @@ __device__ __forceinline__ void lds_barrier()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// LDS byte address of a __shared__ object, as a wave-uniform (scalar) value.
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void *)(p))));
+}
+
+// Global -> LDS copies that bypass registers: every lane's 16 bytes (or its
+// 2 bytes, zero-extended to 4) land at `lds` + lane * 16 (or * 4).  They are
+// issued from inline assembly so that the compiler neither waits on them nor
+// reorders them; completion is awaited explicitly with wait_vmem<N>() before
+// the staged data is read.
+__device__ __forceinline__ void dma_b128(const void *g, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma_u16(const void *g, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_ushort %0, off" ::"v"(g), "s"(lds)
+                 : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmem()
+{
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // Broadcast lane `m` of each 16-lane row to the whole row.
 template <int M>
 __device__ __forceinline__ float row_bcast(float x)
@@ -145,6 +192,10 @@ struct ChunkWave {
     float bias_neg[2];  // head_neg * dt_bias[h][ch] for the two 16-channel tiles
     bf16x8_t sel[2];    // 0/1 selection matrices for the channel-major transposes
     u32x2_t ident;      // 16x16 identity as an x16 B operand
+    float grp_ge[3];    // (g4 >= 1), (g4 >= 2), (g4 >= 3)
+    float grp_le[3];    // (g4 <= 0), (g4 <= 1), (g4 <= 2)
+    float diag_one;     // (l16 == 4 pw + g4): row i equals column j of T
+    float diag_below;   // (l16 >  4 pw + g4)
 
     __device__ int chunk_len(int x) const
     {
@@ -152,19 +203,41 @@ struct ChunkWave {
         return static_cast<int>(left < C ? left : C);
     }
 
-    // Loads are unconditional: a row past the sequence end re-reads the
-    // chunk's first token (always inside the tensors) and is masked later.
-    __device__ void load(int x, RawChunk &r) const
+    // Copy chunk x into LDS slot `slot` (this wave's 32 channels of q, k, g,
+    // v; chunk wave 0 also the 16 beta logits).  Every lane copies something
+    // valid: rows past the sequence end re-read the chunk's first token and
+    // are masked in the gate stage.  kDmaPerChunk copies per wave (+1 beta).
+    static constexpr int kDmaPerChunk = 4;
+    __device__ void fetch(int x, int slot) const
     {
         const int len = chunk_len(x);
-        const int64_t tok = int64_t(x) * C + (l16 < len ? l16 : 0);
-        const int64_t btok = int64_t(x) * C + (lane < len ? lane : 0);
-        r.beta = src_beta[btok * beta_stride];
-        const int64_t e = tok * tok_stride;
-        r.q = *reinterpret_cast<const u32x4_t *>(src_q + e);
-        r.k = *reinterpret_cast<const u32x4_t *>(src_k + e);
-        r.g = *reinterpret_cast<const u32x4_t *>(src_g + e);
-        r.v = *reinterpret_cast<const u32x4_t *>(src_v + e);
+        const int64_t e = (int64_t(x) * C + (l16 < len ? l16 : 0)) * tok_stride;
+        dma_b128(src_q + e, lds_addr(&sh.raw[slot][pw][0][0]));
+        dma_b128(src_k + e, lds_addr(&sh.raw[slot][pw][1][0]));
+        dma_b128(src_g + e, lds_addr(&sh.raw[slot][pw][2][0]));
+        dma_b128(src_v + e, lds_addr(&sh.raw[slot][pw][3][0]));
+        if (pw == 0) {
+            const int64_t btok = int64_t(x) * C + (lane < len ? lane : 0);
+            dma_u16(src_beta + btok * beta_stride, lds_addr(&sh.raw_beta[slot][0]));
+        }
+    }
+    // Wait until the copies of the chunk fetched two fetches ago have landed.
+    __device__ void wait_fetched() const
+    {
+        if (pw == 0)
+            wait_vmem<2 * (kDmaPerChunk + 1)>();
+        else
+            wait_vmem<2 * kDmaPerChunk>();
+    }
+    __device__ RawChunk staged(int slot) const
+    {
+        RawChunk r;
+        r.q = sh.raw[slot][pw][0][lane];
+        r.k = sh.raw[slot][pw][1][lane];
+        r.g = sh.raw[slot][pw][2][lane];
+        r.v = sh.raw[slot][pw][3][lane];
+        r.beta = sh.raw_beta[slot][lane];
+        return r;
     }
 
     // G: gate, decay products and the decayed operands of chunk x.
@@ -183,34 +256,38 @@ struct ChunkWave {
         for (int t = 0; t < 2; ++t) {
             // channel-major tiles: lane (l16, g4) holds tokens 4*g4 + i of
             // channel 32*pw + 16*t + l16
-            f32x4_t cq = mfma32(__builtin_bit_cast(bf16x8_t, r.q), sel[t], zero);
-            f32x4_t ck = mfma32(__builtin_bit_cast(bf16x8_t, r.k), sel[t], zero);
+            const f32x4_t cq = mfma32(__builtin_bit_cast(bf16x8_t, r.q), sel[t], zero);
+            const f32x4_t ck = mfma32(__builtin_bit_cast(bf16x8_t, r.k), sel[t], zero);
             const f32x4_t cg = mfma32(__builtin_bit_cast(bf16x8_t, r.g), sel[t], zero);
-            f32x4_t cv = mfma32(__builtin_bit_cast(bf16x8_t, r.v), sel[t], zero);
+            const f32x4_t cv = mfma32(__builtin_bit_cast(bf16x8_t, r.v), sel[t], zero);
 
-            // rows past the sequence end: no write (k = v = 0), no read-out
-            // (q = 0) and no decay (alpha = 1)
+            // Rows past the sequence end hold a copy of the chunk's first
+            // token.  Only their decay needs masking (alpha = 1): their beta
+            // is 0, which zeroes their rows and columns of T diag(beta) and so
+            // of W, U~ and U; their A, P and output entries are never used.
             float al[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const bool valid = 4 * g4 + i < len;
                 const float e = exp2_f32(fmaf(cg[i], head_neg, bias_neg[t]));
                 const float s = __builtin_amdgcn_rcpf(1.0f + e);
                 const float a = exp2_f32(p.gate_scale * s);
-                al[i] = valid ? a : 1.0f;
-                cq[i] = valid ? cq[i] : 0.0f;
-                ck[i] = valid ? ck[i] : 0.0f;
-                cv[i] = valid ? cv[i] : 0.0f;
+                al[i] = (4 * g4 + i < len) ? a : 1.0f;
             }
             // products within the 4-token group, then across the 4 groups
             const float p0 = al[0], p1 = p0 * al[1], p2 = p1 * al[2], p3 = p2 * al[3];
             const float s3_ = 1.0f, s2_ = al[3], s1_ = al[2] * al[3], s0_ = al[1] * s1_;
             const float P0 = __shfl(p3, l16), P1 = __shfl(p3, l16 + 16),
                         P2 = __shfl(p3, l16 + 32), P3 = __shfl(p3, l16 + 48);
-            const float P01 = P0 * P1, P012 = P01 * P2, gc = P012 * P3;
-            const float P23 = P2 * P3, P123 = P1 * P23;
-            const float pre = g4 == 0 ? 1.0f : (g4 == 1 ? P0 : (g4 == 2 ? P01 : P012));
-            const float suf = g4 == 3 ? 1.0f : (g4 == 2 ? P3 : (g4 == 1 ? P23 : P123));
+            const float gc = ((P0 * P1) * P2) * P3;
+            // products of the group totals before and after this lane's group,
+            // selected exactly with per-lane 0/1 factors f: f * P + (1 - f)
+            // (no lane masks to keep live)
+            const float pre = fmaf(grp_ge[0], P0, 1.0f - grp_ge[0]) *
+                              fmaf(grp_ge[1], P1, 1.0f - grp_ge[1]) *
+                              fmaf(grp_ge[2], P2, 1.0f - grp_ge[2]);
+            const float suf = fmaf(grp_le[2], P3, 1.0f - grp_le[2]) *
+                              fmaf(grp_le[1], P2, 1.0f - grp_le[1]) *
+                              fmaf(grp_le[0], P1, 1.0f - grp_le[0]);
             const float inv_gc = __builtin_amdgcn_rcpf(gc);
             const float gam[4] = {pre * p0, pre * p1, pre * p2, pre * p3};
             const float gbar[4] = {s0_ * suf, s1_ * suf, s2_ * suf, s3_ * suf};
@@ -226,9 +303,10 @@ struct ChunkWave {
             const int ch = 32 * pw + 16 * t + l16;
             const u32x2_t kt2 = pack_bf16x4(kt), qt2 = pack_bf16x4(qt), kb2 = pack_bf16x4(kb),
                           kh2 = pack_bf16x4(kh), v2 = pack_bf16x4(cv);
-            lds_store(&sh.kt_col[s3][ch][4 * g4], kt2);
-            lds_store(&sh.v_col[s3][ch][4 * g4], v2);
-            lds_store(&sh.kb_col[s4][ch][4 * g4], kb2);
+            const int cc = chunk16(ch, g4);
+            lds_store(&sh.kt_col[s3][ch][cc], kt2);
+            lds_store(&sh.v_col[s3][ch][cc], v2);
+            lds_store(&sh.kb_col[s4][ch][cc], kb2);
             if (g4 == 0)
                 sh.gam_c[s4][ch] = gc;
             // token-major copies: (X^T I) puts 4 consecutive channels of one
@@ -260,50 +338,51 @@ struct ChunkWave {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row_i = 4 * g4 + i;
-            sh.amat[pw][row_i][l16] = l16 < row_i ? sh.beta[s2][row_i] * acc[i] : 0.f;
+            sh.amat[row_i][l16] = l16 < row_i ? sh.beta[s2][row_i] * acc[i] : 0.f;
         }
         if (pw == 0) {
             // pacc: lane (i = l16, g4) holds P[i][4*g4 + e]
             f32x4_t pm;
 #pragma unroll
             for (int e = 0; e < 4; ++e) pm[e] = (4 * g4 + e <= l16) ? pacc[e] : 0.f;
-            lds_store(&sh.pmat[s3][l16][4 * g4], pack_bf16x4(pm));
+            lds_store(&sh.pmat[s3][l16][chunk16(l16, g4)], pack_bf16x4(pm));
         }
 
         // T[:, j] for j = 4*pw + g4; lane (g4, l16 = row i).  Right-looking
         // forward substitution: once t_m is known, every later row adds
         // A[i][m] t_m to its running sum.
         const int j = 4 * pw + g4, i = l16;
-        float arow[C];
+        float arow[C];  // A[i][:], zero from column i on
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-            const f32x4_t v = lds_load<f32x4_t>(&sh.amat[pw][i][4 * q4]);
+            const f32x4_t v = lds_load<f32x4_t>(&sh.amat[i][4 * q4]);
             arow[4 * q4 + 0] = v[0];
             arow[4 * q4 + 1] = v[1];
             arow[4 * q4 + 2] = v[2];
             arow[4 * q4 + 3] = v[3];
         }
-        float run = 0.f, t_i = 0.f;
-        solve_steps(arow, j, i, run, t_i);
+        // Lane i keeps run = sum_m A[i][m] t_m; t_i = e_ij - g_ij * run where
+        // e_ij = (i == j) and g_ij = (i > j).  Step m broadcasts t_m from lane
+        // m of each 16-lane row; A[i][m] = 0 for m >= i, so the update needs no
+        // condition.
+        float run = 0.f;
+        solve_steps(arow, run);
+        const float t_i = fmaf(-diag_below, run, diag_one);
         const float tb = t_i * sh.beta[s2][j];
         const __bf16 hi = static_cast<__bf16>(tb);
         const __bf16 lo = static_cast<__bf16>(tb - static_cast<float>(hi));
-        sh.tb_hi[s2][i][j] = __builtin_bit_cast(uint16_t, hi);
-        sh.tb_lo[s2][i][j] = __builtin_bit_cast(uint16_t, lo);
+        // element (i, j) lives in chunk j / 4 = pw at position j % 4 = g4
+        sh.tb_hi[s2][i][chunk16(i, pw) + g4] = __builtin_bit_cast(uint16_t, hi);
+        sh.tb_lo[s2][i][chunk16(i, pw) + g4] = __builtin_bit_cast(uint16_t, lo);
     }
 
     template <int M = 0>
-    __device__ __forceinline__ void solve_steps(const float (&arow)[C], int j, int i, float &run,
-                                                float &t_i) const
+    __device__ __forceinline__ void solve_steps(const float (&arow)[C], float &run) const
     {
         if constexpr (M < C) {
-            const float own = (M == j) ? 1.0f : (M > j ? -run : 0.0f);
-            const float tm = row_bcast<M>(own);
-            if (i == M)
-                t_i = tm;
-            if (i > M)
-                run = fmaf(arow[M], tm, run);
-            solve_steps<M + 1>(arow, j, i, run, t_i);
+            const float tm = row_bcast<M>(fmaf(-diag_below, run, diag_one));
+            run = fmaf(arow[M], tm, run);
+            solve_steps<M + 1>(arow, run);
         }
     }
 
@@ -314,19 +393,19 @@ struct ChunkWave {
         const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
         // lane (l16, g4) holds (T diag(beta))[l16][4*g4 .. 4*g4+3]: the A operand
         // of T diag(beta) V and the B operand of Kt^T (T diag(beta))^T
-        const u32x2_t th = lds_load<u32x2_t>(&sh.tb_hi[s2][l16][4 * g4]);
-        const u32x2_t tl = lds_load<u32x2_t>(&sh.tb_lo[s2][l16][4 * g4]);
+        const u32x2_t th = lds_load<u32x2_t>(&sh.tb_hi[s2][l16][chunk16(l16, g4)]);
+        const u32x2_t tl = lds_load<u32x2_t>(&sh.tb_lo[s2][l16][chunk16(l16, g4)]);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const int ch = 32 * pw + 16 * t + l16;
-            const u32x2_t ka = lds_load<u32x2_t>(&sh.kt_col[s3][ch][4 * g4]);
+            const u32x2_t ka = lds_load<u32x2_t>(&sh.kt_col[s3][ch][chunk16(ch, g4)]);
             f32x4_t w = mfma16(ka, th, zero);
             w = mfma16(ka, tl, w);  // lane (token l16, g4): W[l16][32pw+16t+4g4+i]
             lds_store(&sh.w_row[s2][l16][32 * pw + 16 * t + 4 * g4], pack_bf16x4(w));
-            const u32x2_t vb = lds_load<u32x2_t>(&sh.v_col[s3][ch][4 * g4]);
+            const u32x2_t vb = lds_load<u32x2_t>(&sh.v_col[s3][ch][chunk16(ch, g4)]);
             f32x4_t u = mfma16(th, vb, zero);
             u = mfma16(tl, vb, u);  // lane (vcol, g4): U~[4g4+i][vcol]
-            lds_store(&sh.ut[s2][ch][4 * g4], u);
+            lds_store(&sh.ut[s2][ch][chunk32(ch, g4)], u);
         }
     }
 };
@@ -341,7 +420,7 @@ struct StateWave {
     Shared &sh;
     int64_t t_begin, t_end, chain;
     int w, lane, l16, g4;
-    uint16_t *dst_out;   // out at token t_begin, this lane's 8 value columns
+    uint16_t *dst_out;   // out at token t_begin, value column 32w + 4g4
     int64_t tok_stride;  // H * 128
     f32x4_t S[8][2];     // S[16mt + 4g4 + i][32w + 16nt + l16]
 
@@ -406,6 +485,9 @@ struct StateWave {
             for (int nt = 0; nt < 2; ++nt)
                 sb[kt][nt] = cat8(pack_bf16x4(S[2 * kt][nt]), pack_bf16x4(S[2 * kt + 1][nt]));
 
+        // X = W S (lane (vcol, g4): rows 4g4..4g4+3) and Y^T = S^T Qt^T (lane
+        // (token, g4): value columns 4g4..4g4+3 of the tile), from the same
+        // operand registers with the roles of A and B swapped
         f32x4_t X[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         f32x4_t Y[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -417,39 +499,35 @@ struct StateWave {
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
                 X[nt] = mfma32(wa, sb[kt][nt], X[nt]);
-                Y[nt] = mfma32(qa, sb[kt][nt], Y[nt]);
+                Y[nt] = mfma32(sb[kt][nt], qa, Y[nt]);
             }
         }
 
-        // U = U~ - W S, as bf16 B operands (lane (vcol, g4): tokens 4g4..4g4+3)
+        // U = U~ - W S, as bf16 operands (lane (vcol, g4): tokens 4g4..4g4+3)
         u32x2_t ub[2];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-            const f32x4_t u = lds_load<f32x4_t>(&sh.ut[s2][32 * w + 16 * nt + l16][4 * g4]) - X[nt];
+            const int vc = 32 * w + 16 * nt + l16;
+            const f32x4_t u = lds_load<f32x4_t>(&sh.ut[s2][vc][chunk32(vc, g4)]) - X[nt];
             ub[nt] = pack_bf16x4(u);
         }
 
-        // O = Qt S + P U, staged through LDS for 16-byte row stores
-        const u32x2_t pa = lds_load<u32x2_t>(&sh.pmat[s3][l16][4 * g4]);
+        // O^T = Y^T + U^T P^T; lane (token l16, g4) then holds 4 consecutive
+        // output values of its token and stores them directly
+        const u32x2_t pa = lds_load<u32x2_t>(&sh.pmat[s3][l16][chunk16(l16, g4)]);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-            const f32x4_t o = mfma16(pa, ub[nt], Y[nt]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                sh.ostage[w][4 * g4 + i][16 * nt + l16] = f32_to_bf16_rne(o[i]);
-        }
-        {
-            const int tk = lane >> 2, sg = lane & 3;
-            const u32x4_t ov = lds_load<u32x4_t>(&sh.ostage[w][tk][8 * sg]);
-            if (tk < len)
-                *reinterpret_cast<u32x4_t *>(dst_out + (int64_t(x) * C + tk) * tok_stride) = ov;
+            const f32x4_t o = mfma16(ub[nt], pa, Y[nt]);
+            if (l16 < len)
+                *reinterpret_cast<u32x2_t *>(dst_out + (int64_t(x) * C + l16) * tok_stride + 16 * nt) =
+                    pack_bf16x4(o);
         }
 
         // S <- diag(Gamma_C) S + Kbar^T U
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
             const f32x4_t gc = lds_load<f32x4_t>(&sh.gam_c[s4][16 * mt + 4 * g4]);
-            const u32x2_t ka = lds_load<u32x2_t>(&sh.kb_col[s4][16 * mt + l16][4 * g4]);
+            const u32x2_t ka = lds_load<u32x2_t>(&sh.kb_col[s4][16 * mt + l16][chunk16(l16, g4)]);
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) S[mt][nt] = mfma16(ka, ub[nt], S[mt][nt] * gc);
         }
@@ -474,7 +552,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
 
     if (wave < 4) {
         StateWave<INIT, FINAL> sw{p, sh, t_begin, t_end, chain, wave, lane, l16, g4,
-                                  p.out + first * D + 32 * wave + 8 * (lane & 3), tok_stride, {}};
+                                  p.out + first * D + 32 * wave + 4 * g4, tok_stride, {}};
         sw.load_state();
         int s3 = 0;  // chunk index mod 3 of the chunk being updated
         for (int it = 0; it < n_iter; ++it) {
@@ -513,24 +591,28 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
         cw.ident = u32x2_t{uint32_t(idb[0]) | (uint32_t(idb[1]) << 16),
                            uint32_t(idb[2]) | (uint32_t(idb[3]) << 16)};
     }
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+        cw.grp_ge[q] = g4 >= q + 1 ? 1.0f : 0.0f;
+        cw.grp_le[q] = g4 <= q ? 1.0f : 0.0f;
+    }
+    cw.diag_one = l16 == 4 * pw + g4 ? 1.0f : 0.0f;
+    cw.diag_below = l16 > 4 * pw + g4 ? 1.0f : 0.0f;
     if (n_iter == 0)
         return;
 
     const int nc = static_cast<int>(nchunks);
-    RawChunk raw[kRawSets];
-#pragma unroll
-    for (int s = 0; s < kRawSets - 1; ++s) cw.load(s < nc ? s : nc - 1, raw[s]);
-
+    // chunks 0 and 1 go to slots 0 and 1; iteration `it` fetches chunk it+2
+    cw.fetch(0, 0);
+    cw.fetch(nc > 1 ? 1 : 0, 1);
     // mod-3 slots of the chunks handled by G, SOL and WY in this iteration
     int g3 = 0, sol3 = 2, wy3 = 1;
-    // G runs in every iteration: past the last chunk it only fills LDS slots
-    // that no later stage reads, which keeps the prefetch bookkeeping simple.
-    auto step = [&](int it, RawChunk &cur, RawChunk &next) {
-        cw.gate_stage(it, g3, cur);
-        {
-            const int ahead = it + kRawSets - 1;
-            cw.load(ahead < nc ? ahead : nc - 1, next);
-        }
+    for (int it = 0; it < n_iter; ++it) {
+        // G runs in every iteration: past the last chunk it only fills LDS
+        // slots that no later stage reads.
+        cw.fetch(it + 2 < nc ? it + 2 : nc - 1, sol3);  // slot (it + 2) % 3 == (it - 1) % 3
+        cw.wait_fetched();
+        cw.gate_stage(it, g3, cw.staged(g3));
         if (it >= 1 && it - 1 < nc)
             cw.solve_stage(it - 1, sol3);
         if (it >= 2 && it - 2 < nc)
@@ -539,16 +621,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
         sol3 = sol3 == 2 ? 0 : sol3 + 1;
         wy3 = wy3 == 2 ? 0 : wy3 + 1;
         lds_barrier();
-    };
-    for (int it0 = 0; it0 < n_iter; it0 += kRawSets) {
-        step(it0, raw[0], raw[3]);
-        if (it0 + 1 >= n_iter) break;
-        step(it0 + 1, raw[1], raw[0]);
-        if (it0 + 2 >= n_iter) break;
-        step(it0 + 2, raw[2], raw[1]);
-        if (it0 + 3 >= n_iter) break;
-        step(it0 + 3, raw[3], raw[2]);
     }
+    // no copy may still be writing LDS when the wave ends
+    wait_vmem<0>();
 }
 
 template <int INIT, int FINAL>
