@@ -52,29 +52,29 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int C = kChunk;
 constexpr int D = kHeadDim;
-constexpr int kThreads = 512;
+constexpr int kThreads = 768;  // 4 state waves, 4 gate waves, 4 solve/WY waves
 constexpr int kRawSlots = 3;  // chunks staged in LDS: the one being read + 2 in flight
 
-// LDS bank layout (64 banks of 4 bytes): every access below is arranged so
-// that the lanes served together hit distinct banks.
-//  * Token-major tiles are read and written one token row per lane; their
-//    rows are padded by 16 bytes so the 16 rows fall in different banks.
-//  * 16-element rows (channel-major bf16 tiles, 32 bytes) are accessed in
-//    4-element chunks by lane (row l16, chunk g4); rows r and r + 8 share
-//    banks, so chunk g is stored at g ^ (2 * bit 3 of r).
-//  * 16-element fp32 rows (64 bytes) are accessed in 4-element chunks by
-//    16 lanes at a time; rows r, r+4, r+8, r+12 share banks, so chunk g is
-//    stored at g ^ (bits 2-3 of r).
-constexpr int DP = D + 8;
+// LDS bank layout.  gfx950 serves 64-bit reads 32 lanes at a time from 64
+// banks, 128-bit reads in four passes, and writes 16 lanes at a time into
+// 32 banks.  The tiles below are placed (XOR swizzles measured conflict-free
+// for the access patterns used here) so that lanes served together hit
+// distinct banks:
+//  * token-major tiles [16 tokens][128 channels] are read and written one
+//    token row per lane; the 16-byte chunk c of row r is stored at c ^ r;
+//  * 16-element bf16 rows (channel-major tiles, T diag(beta), P) are accessed
+//    in 4-element chunks; chunk g of row r is stored at g ^ (bits 2-3 of r);
+//  * 16-element fp32 rows (U~) likewise, at g ^ (bits 1-2 of r).
 constexpr int AP = C + 4;  // padded row of the fp32 A matrix
 
-__device__ __forceinline__ int chunk16(int r, int g) { return 4 * (g ^ (((r >> 3) & 1) << 1)); }
-__device__ __forceinline__ int chunk32(int r, int g) { return 4 * (g ^ ((r >> 2) & 3)); }
+__device__ __forceinline__ int tok_off(int r, int e) { return 8 * ((e >> 3) ^ (r & 15)) + (e & 7); }
+__device__ __forceinline__ int chunk16(int r, int g) { return 4 * (g ^ ((r >> 2) & 3)); }
+__device__ __forceinline__ int chunk32(int r, int g) { return 4 * (g ^ ((r >> 1) & 3)); }
 
 struct __align__(16) Shared {
-    uint16_t kt_row[2][C][DP];  // Kt, token-major (bf16)
-    uint16_t kh_row[2][C][DP];  // Kh, token-major
-    uint16_t qt_row[4][C][DP];  // Qt (scale folded in), token-major
+    uint16_t kt_row[2][C][D];  // Kt, token-major (bf16)
+    uint16_t kh_row[2][C][D];  // Kh, token-major
+    uint16_t qt_row[4][C][D];  // Qt (scale folded in), token-major
     uint16_t kt_col[3][D][C];  // Kt, channel-major
     uint16_t v_col[3][D][C];   // V, column-major
     uint16_t kb_col[4][D][C];  // Kbar, channel-major
@@ -84,7 +84,7 @@ struct __align__(16) Shared {
     uint16_t tb_hi[2][C][C];   // T diag(beta) = hi + lo, two bf16 parts
     uint16_t tb_lo[2][C][C];
     uint16_t pmat[3][C][C];    // P
-    uint16_t w_row[2][C][DP];  // W, token-major
+    uint16_t w_row[2][C][D];  // W, token-major
     float ut[2][D][C];         // U~, column-major
     // raw q, k, g, v of a chunk as fetched by each chunk wave (16 bytes per
     // lane, lane order), and the beta logits (zero-extended, chunk wave 0)
@@ -311,7 +311,7 @@ struct ChunkWave {
                 sh.gam_c[s4][ch] = gc;
             // token-major copies: (X^T I) puts 4 consecutive channels of one
             // token in each lane
-            const int col = 32 * pw + 16 * t + 4 * g4;
+            const int col = tok_off(l16, 32 * pw + 16 * t + 4 * g4);
             lds_store(&sh.kt_row[s2][l16][col], pack_bf16x4(mfma16(kt2, ident, zero)));
             lds_store(&sh.kh_row[s2][l16][col], pack_bf16x4(mfma16(kh2, ident, zero)));
             lds_store(&sh.qt_row[s4][l16][col], pack_bf16x4(mfma16(qt2, ident, zero)));
@@ -325,7 +325,7 @@ struct ChunkWave {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, pacc = acc;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
-            const int col = 32 * kt + 8 * g4;
+            const int col = tok_off(l16, 32 * kt + 8 * g4);
             const bf16x8_t a = lds_load<bf16x8_t>(&sh.kt_row[s2][l16][col]);
             const bf16x8_t b = lds_load<bf16x8_t>(&sh.kh_row[s2][l16][col]);
             acc = mfma32(a, b, acc);
@@ -401,7 +401,7 @@ struct ChunkWave {
             const u32x2_t ka = lds_load<u32x2_t>(&sh.kt_col[s3][ch][chunk16(ch, g4)]);
             f32x4_t w = mfma16(ka, th, zero);
             w = mfma16(ka, tl, w);  // lane (token l16, g4): W[l16][32pw+16t+4g4+i]
-            lds_store(&sh.w_row[s2][l16][32 * pw + 16 * t + 4 * g4], pack_bf16x4(w));
+            lds_store(&sh.w_row[s2][l16][tok_off(l16, 32 * pw + 16 * t + 4 * g4)], pack_bf16x4(w));
             const u32x2_t vb = lds_load<u32x2_t>(&sh.v_col[s3][ch][chunk16(ch, g4)]);
             f32x4_t u = mfma16(th, vb, zero);
             u = mfma16(tl, vb, u);  // lane (vcol, g4): U~[4g4+i][vcol]
@@ -492,10 +492,11 @@ struct StateWave {
         f32x4_t Y[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
-            const bf16x8_t wa = cat8(lds_load<u32x2_t>(&sh.w_row[s2][l16][32 * kt + 4 * g4]),
-                                     lds_load<u32x2_t>(&sh.w_row[s2][l16][32 * kt + 16 + 4 * g4]));
-            const bf16x8_t qa = cat8(lds_load<u32x2_t>(&sh.qt_row[s4][l16][32 * kt + 4 * g4]),
-                                     lds_load<u32x2_t>(&sh.qt_row[s4][l16][32 * kt + 16 + 4 * g4]));
+            const int lo = tok_off(l16, 32 * kt + 4 * g4), hi = tok_off(l16, 32 * kt + 16 + 4 * g4);
+            const bf16x8_t wa = cat8(lds_load<u32x2_t>(&sh.w_row[s2][l16][lo]),
+                                     lds_load<u32x2_t>(&sh.w_row[s2][l16][hi]));
+            const bf16x8_t qa = cat8(lds_load<u32x2_t>(&sh.qt_row[s4][l16][lo]),
+                                     lds_load<u32x2_t>(&sh.qt_row[s4][l16][hi]));
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
                 X[nt] = mfma32(wa, sb[kt][nt], X[nt]);
@@ -566,11 +567,32 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
         return;
     }
 
-    const int pw = wave - 4;
+    // waves 4-7 stream chunks in and run the gate stage; waves 8-11 run the
+    // solve and WY stages.  Both kinds own the 32 channels 32*pw..32*pw+31.
+    const bool gate_wave = wave < 8;
+    const int pw = gate_wave ? wave - 4 : wave - 8;
     const int64_t lane_off = first * D + 32 * pw + 8 * g4;
     ChunkWave cw{p, sh, t_begin, t_end, static_cast<int>(nchunks), pw, lane, l16, g4,
                  p.q + lane_off, p.k + lane_off, p.g + lane_off, p.v + lane_off,
                  p.beta + first, tok_stride, p.H};
+    const int nc = static_cast<int>(nchunks);
+
+    if (!gate_wave) {
+        cw.diag_one = l16 == 4 * pw + g4 ? 1.0f : 0.0f;
+        cw.diag_below = l16 > 4 * pw + g4 ? 1.0f : 0.0f;
+        int sol3 = 2, wy3 = 1;  // chunk index mod 3 of the SOL and WY chunks
+        for (int it = 0; it < n_iter; ++it) {
+            if (it >= 1 && it - 1 < nc)
+                cw.solve_stage(it - 1, sol3);
+            if (it >= 2 && it - 2 < nc)
+                cw.wy_stage(it - 2, wy3);
+            sol3 = sol3 == 2 ? 0 : sol3 + 1;
+            wy3 = wy3 == 2 ? 0 : wy3 + 1;
+            lds_barrier();
+        }
+        return;
+    }
+
     const float head_mult = p.A_log ? expf(p.A_log[h]) : 1.0f;
     cw.head_neg = -head_mult * kLog2eF;
 #pragma unroll
@@ -596,30 +618,21 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
         cw.grp_ge[q] = g4 >= q + 1 ? 1.0f : 0.0f;
         cw.grp_le[q] = g4 <= q ? 1.0f : 0.0f;
     }
-    cw.diag_one = l16 == 4 * pw + g4 ? 1.0f : 0.0f;
-    cw.diag_below = l16 > 4 * pw + g4 ? 1.0f : 0.0f;
     if (n_iter == 0)
         return;
 
-    const int nc = static_cast<int>(nchunks);
     // chunks 0 and 1 go to slots 0 and 1; iteration `it` fetches chunk it+2
     cw.fetch(0, 0);
     cw.fetch(nc > 1 ? 1 : 0, 1);
-    // mod-3 slots of the chunks handled by G, SOL and WY in this iteration
-    int g3 = 0, sol3 = 2, wy3 = 1;
+    int g3 = 0;  // chunk index mod 3 of the G chunk
     for (int it = 0; it < n_iter; ++it) {
         // G runs in every iteration: past the last chunk it only fills LDS
         // slots that no later stage reads.
-        cw.fetch(it + 2 < nc ? it + 2 : nc - 1, sol3);  // slot (it + 2) % 3 == (it - 1) % 3
+        const int s_next = g3 == 0 ? 2 : g3 - 1;  // slot (it + 2) % 3
+        cw.fetch(it + 2 < nc ? it + 2 : nc - 1, s_next);
         cw.wait_fetched();
         cw.gate_stage(it, g3, cw.staged(g3));
-        if (it >= 1 && it - 1 < nc)
-            cw.solve_stage(it - 1, sol3);
-        if (it >= 2 && it - 2 < nc)
-            cw.wy_stage(it - 2, wy3);
         g3 = g3 == 2 ? 0 : g3 + 1;
-        sol3 = sol3 == 2 ? 0 : sol3 + 1;
-        wy3 = wy3 == 2 ? 0 : wy3 + 1;
         lds_barrier();
     }
     // no copy may still be writing LDS when the wave ends
