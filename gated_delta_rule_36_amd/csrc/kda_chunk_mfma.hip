@@ -386,29 +386,30 @@ struct ChunkWave {
         }
     }
 
-    // WY: W and U~ for this wave's 32 columns of chunk x.
-    __device__ void wy_stage(int x, int s3) const
-    {
-        const int s2 = x & 1;
-        const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-        // lane (l16, g4) holds (T diag(beta))[l16][4*g4 .. 4*g4+3]: the A operand
-        // of T diag(beta) V and the B operand of Kt^T (T diag(beta))^T
-        const u32x2_t th = lds_load<u32x2_t>(&sh.tb_hi[s2][l16][chunk16(l16, g4)]);
-        const u32x2_t tl = lds_load<u32x2_t>(&sh.tb_lo[s2][l16][chunk16(l16, g4)]);
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int ch = 32 * pw + 16 * t + l16;
-            const u32x2_t ka = lds_load<u32x2_t>(&sh.kt_col[s3][ch][chunk16(ch, g4)]);
-            f32x4_t w = mfma16(ka, th, zero);
-            w = mfma16(ka, tl, w);  // lane (token l16, g4): W[l16][32pw+16t+4g4+i]
-            lds_store(&sh.w_row[s2][l16][tok_off(l16, 32 * pw + 16 * t + 4 * g4)], pack_bf16x4(w));
-            const u32x2_t vb = lds_load<u32x2_t>(&sh.v_col[s3][ch][chunk16(ch, g4)]);
-            f32x4_t u = mfma16(th, vb, zero);
-            u = mfma16(tl, vb, u);  // lane (vcol, g4): U~[4g4+i][vcol]
-            lds_store(&sh.ut[s2][ch][chunk32(ch, g4)], u);
-        }
-    }
 };
+
+// WY: W and U~ for this wave's 32 columns of chunk x.
+__device__ void wy_stage(Shared &sh, int x, int s3, int pw, int l16, int g4)
+{
+    const int s2 = x & 1;
+    const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+    // lane (l16, g4) holds (T diag(beta))[l16][4*g4 .. 4*g4+3]: the A operand
+    // of T diag(beta) V and the B operand of Kt^T (T diag(beta))^T
+    const u32x2_t th = lds_load<u32x2_t>(&sh.tb_hi[s2][l16][chunk16(l16, g4)]);
+    const u32x2_t tl = lds_load<u32x2_t>(&sh.tb_lo[s2][l16][chunk16(l16, g4)]);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int ch = 32 * pw + 16 * t + l16;
+        const u32x2_t ka = lds_load<u32x2_t>(&sh.kt_col[s3][ch][chunk16(ch, g4)]);
+        f32x4_t w = mfma16(ka, th, zero);
+        w = mfma16(ka, tl, w);  // lane (token l16, g4): W[l16][32pw+16t+4g4+i]
+        lds_store(&sh.w_row[s2][l16][tok_off(l16, 32 * pw + 16 * t + 4 * g4)], pack_bf16x4(w));
+        const u32x2_t vb = lds_load<u32x2_t>(&sh.v_col[s3][ch][chunk16(ch, g4)]);
+        f32x4_t u = mfma16(th, vb, zero);
+        u = mfma16(tl, vb, u);  // lane (vcol, g4): U~[4g4+i][vcol]
+        lds_store(&sh.ut[s2][ch][chunk32(ch, g4)], u);
+    }
+}
 
 // ---------------------------------------------------------------------------
 // state waves
@@ -555,12 +556,17 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
         StateWave<INIT, FINAL> sw{p, sh, t_begin, t_end, chain, wave, lane, l16, g4,
                                   p.out + first * D + 32 * wave + 4 * g4, tok_stride, {}};
         sw.load_state();
-        int s3 = 0;  // chunk index mod 3 of the chunk being updated
+        const int nc = static_cast<int>(nchunks);
+        int s3 = 0, wy3 = 1;  // chunk index mod 3 of the updated and the WY chunk
         for (int it = 0; it < n_iter; ++it) {
             if (it >= 3) {
                 sw.chunk(it - 3, s3);
                 s3 = s3 == 2 ? 0 : s3 + 1;
             }
+            // W and U~ of chunk it-2 for this wave's 32 channels / value columns
+            if (it >= 2 && it - 2 < nc)
+                wy_stage(sh, it - 2, wy3, wave, l16, g4);
+            wy3 = wy3 == 2 ? 0 : wy3 + 1;
             lds_barrier();
         }
         sw.store_state();
@@ -580,14 +586,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
     if (!gate_wave) {
         cw.diag_one = l16 == 4 * pw + g4 ? 1.0f : 0.0f;
         cw.diag_below = l16 > 4 * pw + g4 ? 1.0f : 0.0f;
-        int sol3 = 2, wy3 = 1;  // chunk index mod 3 of the SOL and WY chunks
+        int sol3 = 2;  // chunk index mod 3 of the SOL chunk
         for (int it = 0; it < n_iter; ++it) {
             if (it >= 1 && it - 1 < nc)
                 cw.solve_stage(it - 1, sol3);
-            if (it >= 2 && it - 2 < nc)
-                cw.wy_stage(it - 2, wy3);
             sol3 = sol3 == 2 ? 0 : sol3 + 1;
-            wy3 = wy3 == 2 ? 0 : wy3 + 1;
             lds_barrier();
         }
         return;
