@@ -103,6 +103,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="large_b8_t16384_h32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="before warm-up, run one plain device-to-device copy of this many "
+                         "bytes (untimed), as a known-size reference for HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported; this path runs on one GPU "
@@ -124,6 +127,12 @@ def main():
     if final_dtype is not None:
         final = torch.empty(x.num_seqs, H, 128, 128, dtype=final_dtype, device="cuda")
     torch.cuda.synchronize()
+    if args.copy_bytes > 0:
+        src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step():
         kda.fwd(x.q, x.k, x.v, x.g, x.beta, x.scale, out, x.A_log, x.dt_bias, x.lower_bound,
@@ -171,7 +180,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32",
+        "dtype": "bf16",  # bf16 MFMA operands, fp32 accumulation and state
         "data": "synthetic",
         "config": {"workload": args.workload, "B": B, "T": T, "H": H, "K": K, "V": 128,
                    "lower_bound": x.lower_bound, "varlen": x.cu_seqlens is not None,
