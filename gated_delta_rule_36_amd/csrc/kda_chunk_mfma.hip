@@ -173,6 +173,35 @@ __device__ __forceinline__ float row_bcast(float x)
         float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + M, 0xF, 0xF, false));
 }
 
+// Every lane receives x from the lane with the same l16 in each of the four
+// 16-lane rows (r0..r3 = rows 0..3).  v_permlane16_swap exchanges the odd
+// rows of its first operand with the even rows of its second,
+// v_permlane32_swap the upper 32 lanes of its first operand with the lower
+// 32 of its second.  They are issued from inline assembly: with a register
+// and its copy as operands the compiler folds the second result of the
+// builtin into the first.  The s_nop covers the wait states a swap needs
+// after a vector write of its operands.
+__device__ __forceinline__ void swap_rows16(uint32_t &a, uint32_t &b)
+{
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap_rows32(uint32_t &a, uint32_t &b)
+{
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void row_gather(float x, float &r0, float &r1, float &r2, float &r3)
+{
+    uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+    swap_rows16(a, b);  // a: rows {0,0,2,2}, b: rows {1,1,3,3}
+    uint32_t c = a, d = b;
+    swap_rows32(a, c);  // a: {0,0,0,0}, c: {2,2,2,2}
+    swap_rows32(b, d);  // b: {1,1,1,1}, d: {3,3,3,3}
+    r0 = __builtin_bit_cast(float, a);
+    r1 = __builtin_bit_cast(float, b);
+    r2 = __builtin_bit_cast(float, c);
+    r3 = __builtin_bit_cast(float, d);
+}
+
 // ---------------------------------------------------------------------------
 // chunk waves
 // ---------------------------------------------------------------------------
@@ -184,10 +213,17 @@ struct ChunkWave {
     int nchunks;
     int pw;  // 0..3
     int lane, l16, g4;
-    const uint16_t *src_q, *src_k, *src_g, *src_v;  // this lane's 8 channels at token t_begin
-    const uint16_t *src_beta;                       // beta at token t_begin
-    int64_t tok_stride;                             // elements between tokens (H * 128)
-    int64_t beta_stride;                            // H
+    // Fetch addressing.  The bases and strides are wave-uniform (scalar
+    // registers); only the lane offsets are per lane.
+    const char *base_q, *base_k, *base_g, *base_v;  // channel 32 pw of token t_begin
+    const char *base_beta;                          // beta of token t_begin
+    int64_t chunk_bytes;       // between consecutive chunks of q/k/g/v: C * H * 256
+    int64_t beta_chunk_bytes;  // between consecutive chunks of beta: C * H * 2
+    int64_t lane_full;         // lane offset for token l16: l16 * H * 256 + 16 * g4
+    int64_t lane_tail;         // lane offset for a row past the sequence end (token 0)
+    int64_t beta_lane;         // beta lane offset for token `lane`: lane * H * 2
+    uint32_t lds_raw;          // LDS address of raw[0][pw][0][0]
+    uint32_t lds_raw_beta;     // LDS address of raw_beta[0][0]
     float head_neg;     // -exp(A_log[h]) * log2(e)
     float bias_neg[2];  // head_neg * dt_bias[h][ch] for the two 16-channel tiles
     bf16x8_t sel[2];    // 0/1 selection matrices for the channel-major transposes
@@ -208,18 +244,21 @@ struct ChunkWave {
     // valid: rows past the sequence end re-read the chunk's first token and
     // are masked in the gate stage.  kDmaPerChunk copies per wave (+1 beta).
     static constexpr int kDmaPerChunk = 4;
+    static constexpr uint32_t kSlotBytes = sizeof(Shared::raw[0]);
+    static constexpr uint32_t kTensorBytes = sizeof(Shared::raw[0][0][0]);
     __device__ void fetch(int x, int slot) const
     {
         const int len = chunk_len(x);
-        const int64_t e = (int64_t(x) * C + (l16 < len ? l16 : 0)) * tok_stride;
-        dma_b128(src_q + e, lds_addr(&sh.raw[slot][pw][0][0]));
-        dma_b128(src_k + e, lds_addr(&sh.raw[slot][pw][1][0]));
-        dma_b128(src_g + e, lds_addr(&sh.raw[slot][pw][2][0]));
-        dma_b128(src_v + e, lds_addr(&sh.raw[slot][pw][3][0]));
-        if (pw == 0) {
-            const int64_t btok = int64_t(x) * C + (lane < len ? lane : 0);
-            dma_u16(src_beta + btok * beta_stride, lds_addr(&sh.raw_beta[slot][0]));
-        }
+        const int64_t off = l16 < len ? lane_full : lane_tail;
+        const int64_t cb = int64_t(x) * chunk_bytes;
+        const uint32_t m = lds_raw + static_cast<uint32_t>(slot) * kSlotBytes;
+        dma_b128(base_q + cb + off, m);
+        dma_b128(base_k + cb + off, m + kTensorBytes);
+        dma_b128(base_g + cb + off, m + 2 * kTensorBytes);
+        dma_b128(base_v + cb + off, m + 3 * kTensorBytes);
+        if (pw == 0)
+            dma_u16(base_beta + int64_t(x) * beta_chunk_bytes + (lane < len ? beta_lane : 0),
+                    lds_raw_beta + static_cast<uint32_t>(slot) * sizeof(Shared::raw_beta[0]));
     }
     // Wait until the copies of the chunk fetched two fetches ago have landed.
     __device__ void wait_fetched() const
@@ -276,8 +315,8 @@ struct ChunkWave {
             // products within the 4-token group, then across the 4 groups
             const float p0 = al[0], p1 = p0 * al[1], p2 = p1 * al[2], p3 = p2 * al[3];
             const float s3_ = 1.0f, s2_ = al[3], s1_ = al[2] * al[3], s0_ = al[1] * s1_;
-            const float P0 = __shfl(p3, l16), P1 = __shfl(p3, l16 + 16),
-                        P2 = __shfl(p3, l16 + 32), P3 = __shfl(p3, l16 + 48);
+            float P0, P1, P2, P3;
+            row_gather(p3, P0, P1, P2, P3);
             const float gc = ((P0 * P1) * P2) * P3;
             // products of the group totals before and after this lane's group,
             // selected exactly with per-lane 0/1 factors f: f * P + (1 - f)
@@ -547,7 +586,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
     const int64_t nchunks = (t_end - t_begin + C - 1) / C;  // < 2^31 (T is bounded on the host)
     const int n_iter = nchunks > 0 ? static_cast<int>(nchunks) + 3 : 0;
 
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int l16 = lane & 15, g4 = lane >> 4;
     const int64_t tok_stride = p.H * D;
     const int64_t first = (row * p.T + t_begin) * p.H + h;  // token-head row of t_begin
@@ -577,10 +616,17 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
     // solve and WY stages.  Both kinds own the 32 channels 32*pw..32*pw+31.
     const bool gate_wave = wave < 8;
     const int pw = gate_wave ? wave - 4 : wave - 8;
-    const int64_t lane_off = first * D + 32 * pw + 8 * g4;
+    const int64_t wave_off = (first * D + 32 * pw) * 2;  // bytes
+    const int64_t tok_bytes = tok_stride * 2;
     ChunkWave cw{p, sh, t_begin, t_end, static_cast<int>(nchunks), pw, lane, l16, g4,
-                 p.q + lane_off, p.k + lane_off, p.g + lane_off, p.v + lane_off,
-                 p.beta + first, tok_stride, p.H};
+                 reinterpret_cast<const char *>(p.q) + wave_off,
+                 reinterpret_cast<const char *>(p.k) + wave_off,
+                 reinterpret_cast<const char *>(p.g) + wave_off,
+                 reinterpret_cast<const char *>(p.v) + wave_off,
+                 reinterpret_cast<const char *>(p.beta + first),
+                 C * tok_bytes, C * p.H * 2,
+                 l16 * tok_bytes + 16 * g4, 16 * g4, lane * p.H * 2,
+                 lds_addr(&sh.raw[0][pw][0][0]), lds_addr(&sh.raw_beta[0][0])};
     const int nc = static_cast<int>(nchunks);
 
     if (!gate_wave) {
