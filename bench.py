@@ -99,8 +99,9 @@ def cpu_baseline(x, rows: int = 2):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    # the clocks take some 25 launches (about 40 ms) to settle under this load
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="large_b8_t16384_h32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
