@@ -30,9 +30,9 @@
 //                as loaded, token-major).
 //   waves 12-15  solve waves.  Wave 12 forms A, wave 13 P (from the
 //                channel-major tiles, read as token-major operands through
-//                transposing LDS reads); wave 12 + p then solves columns
-//                4p..4p+3 of T and runs the WY stage (W and U~) for channels /
-//                value columns 32p..32p+31.
+//                transposing LDS reads), waves 14 and 15 solve columns 0..7
+//                and 8..15 of T; wave 12 + p then runs the WY stage (W and
+//                U~) for channels / value columns 32p..32p+31.
 // The state and solve waves run at raised issue priority: they carry the
 // serial dependency chains of an iteration, and the gate waves (ample
 // independent work) fill the issue slots they leave.
@@ -50,6 +50,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -175,17 +176,21 @@ __device__ __forceinline__ void wait_vmem()
 // Cross-row swaps: v_permlane16_swap exchanges the odd rows (16 lanes each)
 // of its first operand with the even rows of its second, v_permlane32_swap
 // the upper 32 lanes of its first operand with the lower 32 of its second.
-// They are issued from inline assembly: with a register and its copy as
-// operands the compiler folds the second result of the builtin into the
-// first.  The s_nop covers the wait states a swap needs after a vector write
-// of its operands.
+// (The results are copied out element by element: a __builtin_bit_cast of a
+// vector element reads element 0 with this compiler.)
 __device__ __forceinline__ void swap_rows16(uint32_t &a, uint32_t &b)
 {
-    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    const uint32_t r0 = r[0], r1 = r[1];
+    a = r0;
+    b = r1;
 }
 __device__ __forceinline__ void swap_rows32(uint32_t &a, uint32_t &b)
 {
-    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    const uint32_t r0 = r[0], r1 = r[1];
+    a = r0;
+    b = r1;
 }
 
 // Products over the four 16-lane rows r0..r3 of x (one value per row at the
@@ -352,7 +357,6 @@ struct SolveWave {
     Shared &sh;
     int pw;  // 0..3, wave-uniform
     int l16, g4;
-    float diag_one;  // (l16 == 4 pw + g4): row i equals column j of T
 
     // -A of chunk x: lane (j = l16, g4) gets (Kt Kh^T)[4 g4 + e][j].
     __device__ void a_stage(int x) const
@@ -387,17 +391,19 @@ struct SolveWave {
         lds_store(&sh.pmat[s4][l16][chunk16(l16, g4)], pack_bf16x4(pm));
     }
 
-    // Columns 4 pw .. 4 pw + 3 of T for chunk x, stored as T diag(beta).
+    // Columns 8 (pw - 2) .. 8 (pw - 2) + 7 of T for chunk x (solve waves 2
+    // and 3), stored as T diag(beta).
     __device__ void solve_stage(int x) const
     {
         const int s2 = x & 1, s3 = x % 3;
-        // T[:, j] for j = 4*pw + g4; lane (g4, l16 = row i).  Right-looking
-        // forward substitution on v = e_j - A t: lane i starts from
-        // v_i = (i == j); step m takes t_m = v_m (final once the rows above m
-        // are done; zero for m < j) from lane m of its 16-lane row and
-        // subtracts A[i][m] t_m from every v_i.  A[i][m] = 0 for m >= i, so a
-        // row stops changing once it is final.
-        const int j = 4 * pw + g4, i = l16;
+        // T[:, j] for j = j0, j0 + 1 with j0 = 8 (pw - 2) + 2 g4; lane
+        // (g4, l16 = row i).  Right-looking forward substitution on
+        // v = e_j - A t: lane i starts from v_i = (i == j); step m takes
+        // t_m = v_m (final once the rows above m are done; zero for m < j)
+        // from lane m of its 16-lane row and subtracts A[i][m] t_m from every
+        // v_i.  A[i][m] = 0 for m >= i, so a row stops changing once it is
+        // final.  The two columns run as independent chains.
+        const int j0 = 8 * (pw - 2) + 2 * g4, i = l16;
         float nrow[C];  // -A[i][:], zero from column i on
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
@@ -407,29 +413,35 @@ struct SolveWave {
             nrow[4 * q4 + 2] = v[2];
             nrow[4 * q4 + 3] = v[3];
         }
-        float v = diag_one;
-        solve_steps(nrow, v);
-        const float tb = v * sh.beta[s3][j];
-        const __bf16 hi = static_cast<__bf16>(tb);
-        const __bf16 lo = static_cast<__bf16>(tb - static_cast<float>(hi));
-        // element (i, j) lives in chunk j / 4 = pw at position j % 4 = g4
-        sh.tb_hi[s2][i][chunk16(i, pw) + g4] = __builtin_bit_cast(uint16_t, hi);
-        sh.tb_lo[s2][i][chunk16(i, pw) + g4] = __builtin_bit_cast(uint16_t, lo);
+        float v0 = i == j0 ? 1.0f : 0.0f, v1 = i == j0 + 1 ? 1.0f : 0.0f;
+        solve_steps(nrow, v0, v1);
+        const f32x2_t b2 = lds_load<f32x2_t>(&sh.beta[s3][j0]);
+        const float tb0 = v0 * b2[0];
+        const float tb1 = v1 * b2[1];
+        const __bf16 hi0 = static_cast<__bf16>(tb0), hi1 = static_cast<__bf16>(tb1);
+        const __bf16 lo0 = static_cast<__bf16>(tb0 - static_cast<float>(hi0));
+        const __bf16 lo1 = static_cast<__bf16>(tb1 - static_cast<float>(hi1));
+        // elements (i, j0), (i, j0 + 1): chunk j0 / 4, positions j0 % 4, + 1
+        const int pos = chunk16(i, j0 >> 2) + (j0 & 3);
+        lds_store(&sh.tb_hi[s2][i][pos], pack_bf16x2(static_cast<float>(hi0), static_cast<float>(hi1)));
+        lds_store(&sh.tb_lo[s2][i][pos], pack_bf16x2(static_cast<float>(lo0), static_cast<float>(lo1)));
     }
 
-    // One multiply-add per step, with t_m read straight from lane m of the
-    // row through the DPP broadcast of the first source (the compiler emits a
-    // separate move for the builtin form).  The s_nop gives the two wait
-    // states a DPP read needs after the vector write of its source.  Step 15
-    // is skipped: A[i][15] = 0 for every row.
+    // One multiply-add per step and column, with t_m read straight from lane
+    // m of the row through the DPP broadcast of the first source (the
+    // compiler emits a separate move for the builtin form).  The s_nop gives
+    // the two wait states a DPP read needs after the vector write of its
+    // source.  Step 15 is skipped: A[i][15] = 0 for every row.
     template <int M = 0>
-    __device__ __forceinline__ void solve_steps(const float (&nrow)[C], float &v) const
+    __device__ __forceinline__ void solve_steps(const float (&nrow)[C], float &v0, float &v1) const
     {
         if constexpr (M < C - 1) {
-            asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %0, %1 row_newbcast:%2 row_mask:0xf bank_mask:0xf"
-                         : "+v"(v)
+            asm volatile("s_nop 1\n\t"
+                         "v_fmac_f32_dpp %0, %0, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf\n\t"
+                         "v_fmac_f32_dpp %1, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                         : "+v"(v0), "+v"(v1)
                          : "v"(nrow[M]), "n"(M));
-            solve_steps<M + 1>(nrow, v);
+            solve_steps<M + 1>(nrow, v0, v1);
         }
     }
 
@@ -612,16 +624,17 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
 
     if (wave >= 12) {
         const int pw = wave - 12;
-        const SolveWave sv{sh, pw, l16, g4, l16 == 4 * pw + g4 ? 1.0f : 0.0f};
+        const SolveWave sv{sh, pw, l16, g4};
         __builtin_amdgcn_s_setprio(3);
         for (int it = 0; it < n_iter; ++it) {
-            if (it >= 1 && it - 1 < nc) {
-                if (pw == 0)
-                    sv.a_stage(it - 1);
-                else if (pw == 1)
-                    sv.p_stage(it - 1);
-            }
-            if (it >= 2 && it - 2 < nc)
+            if (pw < 2) {
+                if (it >= 1 && it - 1 < nc) {
+                    if (pw == 0)
+                        sv.a_stage(it - 1);
+                    else
+                        sv.p_stage(it - 1);
+                }
+            } else if (it >= 2 && it - 2 < nc)
                 sv.solve_stage(it - 2);
             if (it >= 3 && it - 3 < nc)
                 sv.wy_stage(it - 3);
@@ -661,6 +674,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
     // it (loaded two iterations earlier), runs the gate stage on it and
     // reloads the set with chunk it + 2.  Past the last chunk the stage runs
     // on a repeat of it and fills only ring slots that no later stage reads.
+    // The state and solve waves (priority 3) sit on the critical path; the
+    // gate waves fill the issue slots they leave.
+    __builtin_amdgcn_s_setprio(1);
     RawRegs ra{}, rb{};
     gw.issue(ra, 0);
     asm volatile("" ::: "memory");  // keep the two sets' loads in order
