@@ -51,7 +51,7 @@ extern "C" kda_status kda_fwd(const void *q, const void *k, const void *v, const
         return KDA_ERR_LOWER_BOUND;
     if (!std::isfinite(scale))
         return KDA_ERR_SCALE;
-    if (B < 1 || H < 1 || T < 0 || T > INT32_MAX)
+    if (B < 1 || H < 1 || H > 65536 || T < 0 || T > INT32_MAX)
         return KDA_ERR_SIZE;
     if (cu_seqlens && (B != 1 || num_seqs < 0))
         return KDA_ERR_VARLEN_BATCH;
@@ -133,7 +133,7 @@ extern "C" const char *kda_status_string(kda_status status)
     case KDA_ERR_VARLEN_BATCH: return "cu_seqlens requires B == 1 and num_seqs >= 0";
     case KDA_ERR_STATE_DTYPE: return "state dtype must be bf16 or fp32, and match between initial and final";
     case KDA_ERR_ALIAS: return "an output buffer overlaps an input buffer";
-    case KDA_ERR_SIZE: return "bad size (B, H >= 1, T >= 0, no int64 overflow)";
+    case KDA_ERR_SIZE: return "bad size (B >= 1, 1 <= H <= 65536, 0 <= T < 2^31, no int64 overflow)";
     case KDA_ERR_SCALE: return "scale must be finite";
     case KDA_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
     }

@@ -22,17 +22,21 @@
 //                update.  S is the B operand of W S and Qt S through a fixed
 //                permutation of the contraction index, so the fp32
 //                accumulators convert to bf16 operands in place.
-//   waves 4-11   gate waves.  Wave 4 + c owns channels 16c..16c+15: it loads
-//                q, k, g, v and beta straight into registers two chunks ahead,
-//                transposes q, k, g to channel-major with an MFMA against the
-//                identity, computes the gate, the cumulative decay products
-//                and the decayed operands, and stores them channel-major (v
-//                as loaded, token-major).
-//   waves 12-15  solve waves.  Wave 12 forms A, wave 13 P (from the
-//                channel-major tiles, read as token-major operands through
-//                transposing LDS reads), waves 14 and 15 solve columns 0..7
-//                and 8..15 of T; wave 12 + p then runs the WY stage (W and
-//                U~) for channels / value columns 32p..32p+31.
+//   waves 4-11   gate waves.  Loads: every gate wave moves a quarter-tensor
+//                slab (8 token rows of q, k, g or v) of each chunk straight
+//                into LDS with direct global-to-LDS loads two chunks ahead,
+//                whole 128-byte lines per request (q, k, g into a staging
+//                ring, v into its ring for the WY stage).  Compute: wave 4 + c
+//                owns channels 16c..16c+15: it reads its q, k, g channel-major
+//                through transposing LDS reads, computes the gate, the
+//                cumulative decay products and the decayed operands, and
+//                stores them channel-major.
+//   waves 12-15  solve waves.  Wave 12 loads beta two chunks ahead and forms
+//                A, wave 13 P (from the channel-major tiles, read as
+//                token-major operands through transposing LDS reads), waves
+//                14 and 15 solve columns 0..7 and 8..15 of T; wave 12 + p then
+//                runs the WY stage (W and U~) for channels / value columns
+//                32p..32p+31.
 // The state and solve waves run at raised issue priority: they carry the
 // serial dependency chains of an iteration, and the gate waves (ample
 // independent work) fill the issue slots they leave.
@@ -40,6 +44,8 @@
 // solve of chunk it-2, WY of chunk it-3 and the state update of chunk it-4;
 // one workgroup barrier per iteration orders every hand-off through LDS.
 #include <hip/hip_runtime.h>
+
+#include <cstddef>
 
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -59,6 +65,7 @@ constexpr int C = kChunk;
 constexpr int D = kHeadDim;
 constexpr int kThreads = 1024;  // 4 state waves, 8 gate waves, 4 solve waves
 constexpr int kStages = 4;      // iterations between the gate and the state stage of a chunk
+constexpr int kLoadsPerChunk = 2;  // DMAs per gate wave and chunk
 
 // LDS bank layout.  gfx950 serves 64-bit reads 32 lanes at a time from 64
 // banks, 128-bit reads in four passes, and writes 16 lanes at a time into
@@ -70,12 +77,62 @@ constexpr int kStages = 4;      // iterations between the gate and the state sta
 //  * 16-element bf16 rows (channel-major tiles, T diag(beta), P) are accessed
 //    in 4-element chunks; chunk g of row r is stored at g ^ (bits 2-3 of r);
 //  * 16-element fp32 rows (U~) likewise, at g ^ (bits 1-2 of r);
-//  * 16 x 16 fp32 matrices use a row pitch of 20 floats.
+//  * 16 x 16 fp32 matrices use a row pitch of 20 floats;
+//  * W rows are padded to 272 bytes instead (no swizzle), with the channels
+//    of each 32-channel block kt stored in the order the state stage reads
+//    them: 16-byte chunk 4 kt + g holds channels 32kt + 4g .. 32kt + 4g + 3
+//    and 32kt + 16 + 4g .. 32kt + 16 + 4g + 3.
 constexpr int AP = C + 4;
+constexpr int kWPitch = D + 8;  // bf16 elements per W row
 
 __device__ __forceinline__ int tok_off(int r, int e) { return 8 * ((e >> 3) ^ (r & 15)) + (e & 7); }
 __device__ __forceinline__ int chunk16(int r, int g) { return 4 * (g ^ ((r >> 2) & 3)); }
 __device__ __forceinline__ int chunk32(int r, int g) { return 4 * (g ^ ((r >> 1) & 3)); }
+
+// Hot-loop LDS accesses go through 32-bit LDS byte addresses: a per-lane
+// base computed once, plus the ring slot's offset (one add per chunk), plus
+// a constant that the compiler folds into the instruction's offset field.
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_u8 *)p));
+}
+// A per-chunk base address (lane base + ring slot) kept in one register:
+// without the empty asm the compiler re-associates base + slot + constant
+// and keeps one hoisted base per constant, paying an add per access.
+__device__ __forceinline__ uint32_t slot_base(uint32_t a)
+{
+    asm("" : "+v"(a));
+    return a;
+}
+template <typename V>
+__device__ __forceinline__ V lds_ld(uint32_t a)
+{
+    return *(const __attribute__((address_space(3))) V *)(uintptr_t)a;
+}
+template <typename V>
+__device__ __forceinline__ void lds_st(uint32_t a, V v)
+{
+    *(__attribute__((address_space(3))) V *)(uintptr_t)a = v;
+}
+// Byte offset, within a channel-major bf16 tile, of the address lane
+// (l16, g4) passes to the transposing read that yields the token-major
+// operand of channels c0 .. c0 + 15 (c0 a multiple of 16; add c0 * 2 C).
+__device__ __forceinline__ uint32_t tok_lane(int l16, int g4)
+{
+    return 2 * ((4 * g4 + (l16 >> 2)) * C + 4 * ((l16 & 3) ^ g4));
+}
+// Byte offset of lane (l16, g4)'s four elements in row l16 of a 16-wide
+// bf16 tile (chunk16 swizzle); row 16 m + l16 adds 512 m.
+__device__ __forceinline__ uint32_t row16_lane(int l16, int g4)
+{
+    return 2 * (l16 * C + chunk16(l16, g4));
+}
+// The same for 16-wide fp32 rows (chunk32 swizzle).
+__device__ __forceinline__ uint32_t row32_lane(int l16, int g4)
+{
+    return 4 * (l16 * C + chunk32(l16, g4));
+}
 
 // Ring buffers between the stages; a tile written for chunk x lives in slot
 // x mod (its ring size), which is sized to outlive its last reader.
@@ -83,7 +140,7 @@ struct __align__(16) Shared {
     uint16_t kt_col[4][D][C];  // Kt, channel-major; read by A and WY
     uint16_t kh_col[2][D][C];  // Kh, channel-major; read by A and P
     uint16_t qt_col[5][D][C];  // Qt (scale folded in), channel-major; read by P and the state stage
-    uint16_t v_row[4][C][D];   // V as loaded, token-major; read by WY
+    uint16_t v_row[6][C][D];   // V as loaded (DMA), token-major; read by WY
     uint16_t kb_col[5][D][C];  // Kbar, channel-major; read by the state stage
     float gam_c[5][D];         // Gamma_C per channel
     float beta[3][C];          // sigmoid(beta logits), 0 on padding rows
@@ -91,9 +148,25 @@ struct __align__(16) Shared {
     uint16_t pmat[4][C][C];    // P (bf16), lower
     uint16_t tb_hi[2][C][C];   // T diag(beta) = hi + lo, two bf16 parts
     uint16_t tb_lo[2][C][C];
-    uint16_t w_row[2][C][D];   // W, token-major
+    uint16_t w_row[2][C][kWPitch];  // W, token-major, padded rows
     float ut[2][D][C];         // U~, column-major
+    uint16_t stage[3][3][C][D];  // q, k, g as loaded (DMA), token-major; read by the gate stage
 };
+
+// Byte offsets of the rings within Shared, and the bytes of one ring slot.
+constexpr uint32_t kOffKt = offsetof(Shared, kt_col), kOffKh = offsetof(Shared, kh_col);
+constexpr uint32_t kOffQt = offsetof(Shared, qt_col), kOffV = offsetof(Shared, v_row);
+constexpr uint32_t kOffKb = offsetof(Shared, kb_col), kOffGam = offsetof(Shared, gam_c);
+constexpr uint32_t kOffBeta = offsetof(Shared, beta), kOffA = offsetof(Shared, amat);
+constexpr uint32_t kOffP = offsetof(Shared, pmat), kOffThi = offsetof(Shared, tb_hi);
+constexpr uint32_t kOffTlo = offsetof(Shared, tb_lo), kOffW = offsetof(Shared, w_row);
+constexpr uint32_t kOffU = offsetof(Shared, ut), kOffStage = offsetof(Shared, stage);
+constexpr uint32_t kTile = D * C * 2;          // bf16 [D][C] or [C][D] tile
+constexpr uint32_t kTileW = C * kWPitch * 2;   // W tile
+constexpr uint32_t kTileU = D * C * 4;         // U~ tile (fp32)
+constexpr uint32_t kTileCC = C * C * 2;        // 16 x 16 bf16 (P, T parts)
+constexpr uint32_t kTileA = C * AP * 4;        // -A (fp32)
+constexpr uint32_t kTileGam = D * 4, kTileBeta = C * 4;
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
 {
@@ -103,6 +176,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
 __device__ __forceinline__ u32x2_t pack_bf16x4(f32x4_t x)
 {
     return u32x2_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+}
+__device__ __forceinline__ f32x4_t bf16x4_to_f32(u32x2_t t)
+{
+    const uint32_t a = t[0], b = t[1];
+    return f32x4_t{__uint_as_float(a << 16), __uint_as_float(a & 0xffff0000u), __uint_as_float(b << 16),
+                   __uint_as_float(b & 0xffff0000u)};
 }
 __device__ __forceinline__ f32x4_t mfma32(bf16x8_t a, bf16x8_t b, f32x4_t c)
 {
@@ -117,47 +196,36 @@ __device__ __forceinline__ bf16x8_t cat8(u32x2_t lo, u32x2_t hi)
 {
     return __builtin_bit_cast(bf16x8_t, u32x4_t{lo[0], lo[1], hi[0], hi[1]});
 }
-template <typename V>
-__device__ __forceinline__ V lds_load(const void *p)
-{
-    return *static_cast<const V *>(p);
-}
-template <typename V>
-__device__ __forceinline__ void lds_store(void *p, V v)
-{
-    *static_cast<V *>(p) = v;
-}
 
-// Transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane row, lane
-// L supplies the four bf16 at its address, X[L][0..3], and lane i receives
-// X[4r + i/4][i%4] for r = 0..3.  With lane L of row g4 pointing at tokens
-// 4(L%4)..4(L%4)+3 of channel c0 + 4 g4 + L/4 of a channel-major tile, lane
-// (token i, g4) receives channels c0 + 4 g4 .. c0 + 4 g4 + 3 of token i: the
-// token-major operand of an MFMA that contracts over channels.
-__device__ __forceinline__ u32x2_t tok_operand(const uint16_t (&col)[D][C], int c0, int l16, int g4)
+// Transposing LDS read (ds_read_b64_tr_b16) at LDS byte address a.  Within
+// each 16-lane row, lane L supplies the four bf16 at its address, X[L][0..3],
+// and lane i receives X[4r + i/4][i%4] for r = 0..3.
+//  * On a channel-major tile, with lane L of row g4 pointing at tokens
+//    4(L%4)..4(L%4)+3 of channel c0 + 4 g4 + L/4 (address tok_lane + 2 C c0),
+//    lane (token i, g4) receives channels c0 + 4 g4 .. c0 + 4 g4 + 3 of token
+//    i: the token-major operand of an MFMA that contracts over channels.
+//  * On a token-major tile, with lane L of row g4 pointing at channels
+//    c0 + 4(L%4) .. c0 + 4(L%4) + 3 of token 4 g4 + L/4, lane (l16, g4)
+//    receives tokens 4 g4 .. 4 g4 + 3 of channel c0 + l16: the channel-major
+//    operand of an MFMA that contracts over tokens.
+__device__ __forceinline__ u32x2_t lds_tr(uint32_t a)
 {
-    const int c = c0 + 4 * g4 + (l16 >> 2);
-    const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4_t *)(&col[c][chunk16(c, l16 & 3)]));
-    return __builtin_bit_cast(u32x2_t, v);
+    return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                           (__attribute__((address_space(3))) s16x4_t *)(uintptr_t)a));
 }
-// The same read on a token-major tile: with lane L of row g4 pointing at
-// channels c0 + 4(L%4) .. c0 + 4(L%4) + 3 of token 4 g4 + L/4, lane (l16, g4)
-// receives tokens 4 g4 .. 4 g4 + 3 of channel c0 + l16: the channel-major
-// operand of an MFMA that contracts over tokens.
-__device__ __forceinline__ u32x2_t chan_operand(const uint16_t (&row)[C][D], int c0, int l16, int g4)
+// Eight channels per lane for a 16x16x32 operand over channels c0..c0+31 of
+// a channel-major tile (a = tile + tok_lane + 2 C c0): contraction slot
+// 8 g4 + e is channel c0 + 4 g4 + e (e < 4) and c0 + 16 + 4 g4 + (e - 4).
+__device__ __forceinline__ bf16x8_t lds_tr32(uint32_t a)
+{
+    return cat8(lds_tr(a), lds_tr(a + 32 * C));
+}
+// Lane part of the transposing read of channels c0 + 4(L%4).. of token
+// 4 g4 + L/4 in a token-major [C][D] tile (tok_off swizzle).
+__device__ __forceinline__ uint32_t chan_lane(int c0, int l16, int g4)
 {
     const int r = 4 * g4 + (l16 >> 2);
-    const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4_t *)(&row[r][tok_off(r, c0 + 4 * (l16 & 3))]));
-    return __builtin_bit_cast(u32x2_t, v);
-}
-// Eight channels per lane for a 16x16x32 operand over channels 32kt..32kt+31:
-// contraction slot 8 g4 + e is channel 32kt + 4 g4 + e (e < 4) and
-// 32kt + 16 + 4 g4 + (e - 4) (e >= 4).
-__device__ __forceinline__ bf16x8_t tok_operand32(const uint16_t (&col)[D][C], int kt, int l16, int g4)
-{
-    return cat8(tok_operand(col, 32 * kt, l16, g4), tok_operand(col, 32 * kt + 16, l16, g4));
+    return 2 * (r * D + tok_off(r, c0 + 4 * (l16 & 3)));
 }
 
 // Workgroup barrier that orders LDS only.  Outstanding global loads (the
@@ -215,100 +283,92 @@ __device__ __forceinline__ void row_products(float x, float fh, float fo, float 
 // gate waves
 // ---------------------------------------------------------------------------
 
-// One chunk of a gate wave's inputs, loaded straight into registers: per
-// lane one token (l16) and 4 consecutive channels (16c + 4 g4 ..) of q, k,
-// g, v, and (lane < 16) the bf16 beta logit of token `lane` in the low half
-// of `beta`.
-struct RawRegs {
-    u32x2_t q, k, g, v;
-    uint32_t beta;
-};
-
-// Plain loads: the compiler tracks them and waits (s_waitcnt vmcnt) right
-// before the first use of each register set, leaving the loads of the other
-// set in flight.
-__device__ __forceinline__ u32x2_t gload_b64(const char *p)
-{
-    return *reinterpret_cast<const u32x2_t *>(p);
-}
+// Plain load (the beta logits): the compiler tracks it and waits (s_waitcnt
+// vmcnt) right before the first use of the register.
 __device__ __forceinline__ uint32_t gload_u16(const char *p)
 {
     return *reinterpret_cast<const uint16_t *>(p);
 }
 
+// Direct global-to-LDS load (global_load_lds_dwordx4): lane i's 16 bytes,
+// read at base + voff, land at LDS byte address dst + 16 i (dst is
+// wave-uniform and goes in M0).  Written as asm so that the compiler does not
+// make later, unrelated LDS accesses wait for it; the issuing wave waits
+// (vmcnt) before the barrier that hands the data to the other waves.
+__device__ __forceinline__ void dma16(const char *base, uint32_t voff, uint32_t dst)
+{
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(dst) : "memory");
+}
+
 struct GateWave {
     const FwdParams &p;
-    Shared &sh;
-    int64_t t_begin, t_end;
     int gc16;  // 0..7: channels 16 gc16 .. 16 gc16 + 15, wave-uniform
     int lane, l16, g4;
-    // Load addressing.  The bases and strides are wave-uniform (scalar
-    // registers); only the lane offsets are per lane.
-    const char *base_q, *base_k, *base_g, *base_v;  // channel 16 gc16 of token t_begin
-    const char *base_beta;                          // beta of token t_begin
-    int64_t chunk_bytes;       // between consecutive chunks of q/k/g/v: C * H * 256
-    int64_t beta_chunk_bytes;  // between consecutive chunks of beta: C * H * 2
-    int64_t lane_full;         // lane offset for token l16: l16 * H * 256 + 8 * g4
-    int64_t lane_tail;         // lane offset for a row past the sequence end (token 0)
-    int64_t beta_lane;         // beta lane offset for token `lane`: lane * H * 2
+    int n_full, tail;  // full chunks of the sequence; length of a partial last chunk (0: none)
+    // Loads.  Gate wave gc16 moves rows 8 hf .. 8 hf + 7 (hf = gc16 & 1) of
+    // tensor gc16 / 2 (q, k, g, v) of every chunk into LDS, 4 rows (1 KB) per
+    // DMA: lane i takes 16-byte chunk (i % 16) ^ r of row r = 4 j + i / 16 of
+    // its pair, which lands at position i % 16 of the row: the swizzled
+    // token-major layout.  Rows past the sequence end take token 0's data.
+    // Bases and strides are wave-uniform (scalar registers).
+    const char *dma_src;       // the tensor at token t_begin
+    int64_t chunk_bytes;       // between consecutive chunks: C * H * 256
+    uint32_t dma_full[2];      // lane offsets of the two DMAs
+    uint32_t dma_tail[2];      // the same with rows past the end of a partial chunk on token 0
+    uint32_t dma_dst;          // LDS byte address of row 8 hf in slot 0 of the ring
+    uint32_t dma_slot;         // bytes between ring slots (stage or V ring)
+    int dma_ring;              // 3 (stage) or 6 (V ring)
+    // LDS addresses (ring slot 0, without the ring's offset): this lane's
+    // transposing read of channels 16 gc16 + 4 (l16 % 4) .. of token
+    // 4 g4 + l16 / 4 in the stage tiles; its stores into the channel-major
+    // tiles (channel 16 gc16 + l16, tokens 4 g4 ..) and of Gamma_C.
+    uint32_t rd_stage, st_col, st_gam;
     float head_neg;  // -exp(A_log[h]) * log2(e)
     float bias_neg;  // head_neg * dt_bias[h][16 gc16 + l16]
-    u32x2_t ident;   // 16x16 identity as an x16 operand
     float grp_hi;   // (g4 >= 2)
     float grp_odd;  // (g4 odd)
 
-    __device__ int chunk_len(int x) const
-    {
-        const int64_t left = t_end - (t_begin + int64_t(x) * C);
-        return static_cast<int>(left < C ? left : C);
-    }
+    __device__ int chunk_len(int x) const { return x < n_full ? C : tail; }
 
-    // Start loading chunk x into r.  Every lane loads something valid: rows
-    // past the sequence end re-read the chunk's first token and are masked
-    // in the gate stage.
-    __device__ void issue(RawRegs &r, int x) const
+    // Start loading chunk x: two DMAs (kLoadsPerChunk) into its ring slot.
+    // Every lane loads something valid.
+    __device__ void issue(int x) const
     {
-        const int len = chunk_len(x);
-        const int64_t off = (len >= C || l16 < len) ? lane_full : lane_tail;
-        const int64_t cb = int64_t(x) * chunk_bytes;
-        r.q = gload_b64(base_q + cb + off);
-        r.k = gload_b64(base_k + cb + off);
-        r.g = gload_b64(base_g + cb + off);
-        r.v = gload_b64(base_v + cb + off);
-        r.beta = gload_u16(base_beta + int64_t(x) * beta_chunk_bytes + (lane < len ? beta_lane : 0));
+        uint32_t o0 = dma_full[0], o1 = dma_full[1];
+        if (x >= n_full) {
+            o0 = dma_tail[0];
+            o1 = dma_tail[1];
+        }
+        const char *src = dma_src + int64_t(x) * chunk_bytes;
+        const uint32_t dst = dma_dst + static_cast<uint32_t>(dma_ring == 6 ? x % 6 : x % 3) * dma_slot;
+        dma16(src, o0, dst);
+        dma16(src, o1, dst + 1024);
     }
 
     // Gate, decay products and decayed operands of chunk x for this wave's
     // 16 channels.  FULL: all 16 rows of the chunk lie in the sequence.
-    __device__ void gate_stage(int x, const RawRegs &r) const
+    __device__ void gate_stage(int x) const
     {
-        if (chunk_len(x) >= C)
-            gate_rows<true>(x, r);
+        if (x < n_full)
+            gate_rows<true>(x);
         else
-            gate_rows<false>(x, r);
+            gate_rows<false>(x);
     }
     template <bool FULL>
-    __device__ void gate_rows(int x, const RawRegs &r) const
+    __device__ void gate_rows(int x) const
     {
-        const int len = chunk_len(x);
-        const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-        const int s2 = x & 1, s3 = x % 3, s4 = x & 3, s5 = x % 5;
-        // beta (gate wave 0; every gate wave loads it, so that all of them
-        // keep the same number of loads in flight)
-        if (gc16 == 0) {
-            const float b = sigmoid_f32(bf16_to_f32(static_cast<uint16_t>(r.beta)));
-            if (lane < C)
-                sh.beta[s3][lane] = (FULL || lane < len) ? b : 0.f;
-        }
-
-        // channel-major: (X I) with X token-major puts tokens 4 g4 .. 4 g4 + 3
-        // of channel 16 gc16 + l16 in lane (l16, g4)
-        const f32x4_t cq = mfma16(r.q, ident, zero);
-        const f32x4_t ck = mfma16(r.k, ident, zero);
-        const f32x4_t cg = mfma16(r.g, ident, zero);
+        const int len = FULL ? C : tail;
+        const uint32_t s2 = x & 1, s3 = x % 3, s4 = x & 3, s5 = x % 5;
+        // channel-major: the transposing read of the token-major stage tiles
+        // gives lane (l16, g4) tokens 4 g4 .. 4 g4 + 3 of channel 16 gc16 + l16
+        const uint32_t ar = slot_base(rd_stage + s3 * (3 * kTile));
+        const f32x4_t cq = bf16x4_to_f32(lds_tr(ar));
+        const f32x4_t ck = bf16x4_to_f32(lds_tr(ar + kTile));
+        const f32x4_t cg = bf16x4_to_f32(lds_tr(ar + 2 * kTile));
 
         // Rows past the sequence end hold a copy of the chunk's first token.
-        // Only their decay needs masking (alpha = 1): their beta is 0, which
+        // Only their decay needs masking (alpha = 1): their beta is 0 (set by
+        // the solve wave that loads beta), which
         // zeroes their rows and columns of T diag(beta) and so of W, U~ and
         // U; their A, P and output entries are never used.
         float al[4];
@@ -338,14 +398,13 @@ struct GateWave {
             kb[i] = ck[i] * gbar[i];
             kh[i] = kb[i] * inv_gc;
         }
-        const int ch = 16 * gc16 + l16, cc = chunk16(ch, g4);
-        lds_store(&sh.kt_col[s4][ch][cc], pack_bf16x4(kt));
-        lds_store(&sh.kh_col[s2][ch][cc], pack_bf16x4(kh));
-        lds_store(&sh.qt_col[s5][ch][cc], pack_bf16x4(qt));
-        lds_store(&sh.v_row[s4][l16][tok_off(l16, 16 * gc16 + 4 * g4)], r.v);
-        lds_store(&sh.kb_col[s5][ch][cc], pack_bf16x4(kb));
+        const uint32_t a5 = slot_base(st_col + s5 * kTile);  // Qt and Kbar share the ring index
+        lds_st(slot_base(st_col + s4 * kTile) + kOffKt, pack_bf16x4(kt));
+        lds_st(slot_base(st_col + s2 * kTile) + kOffKh, pack_bf16x4(kh));
+        lds_st(a5 + kOffQt, pack_bf16x4(qt));
+        lds_st(a5 + kOffKb, pack_bf16x4(kb));
         if (g4 == 0)
-            sh.gam_c[s5][ch] = gc;
+            lds_st(st_gam + s5 * kTileGam, gc);
     }
 };
 
@@ -354,24 +413,56 @@ struct GateWave {
 // ---------------------------------------------------------------------------
 
 struct SolveWave {
-    Shared &sh;
     int pw;  // 0..3, wave-uniform
     int l16, g4;
+    // LDS addresses (ring slot 0, without the ring's offset) of this lane's
+    // accesses: tok = sh + tok_lane; r16 = sh + row16_lane; amat_st: -A
+    // entries (4 g4 + e, l16); amat_ld: row l16 of -A; bt: beta of tokens
+    // 4 g4 .. 4 g4 + 3 (wave 0) or of the column pair j0, j0 + 1 (waves 2, 3);
+    // tb_st: T diag(beta) entries (l16, j0 .. j0 + 1); wy_k: Kt channel
+    // 32 pw + l16; wy_w: W row l16, chunk 4 pw + g4; wy_v0/1: V operands
+    // of channels 32 pw and 32 pw + 16; wy_u: U~ column 32 pw + l16.
+    uint32_t tok, r16, amat_st, amat_ld, bt, tb_st, wy_k, wy_w, wy_v0, wy_v1, wy_u;
+    // Beta (wave 0): logits of token `lane` (lane < 16) of each chunk, loaded
+    // two iterations ahead of their use; st_beta = the lane's LDS entry.
+    int lane, n_full, tail;
+    const char *base_beta;     // beta of token t_begin
+    int64_t beta_chunk_bytes;  // C * H * 2
+    uint32_t beta_lane;        // lane * H * 2 (lane < 16), else 0
+    uint32_t st_beta;
+
+    // The beta logits of chunk x (rows past the end read token 0).
+    __device__ uint32_t load_beta(int x) const
+    {
+        uint32_t off = beta_lane;
+        if (x >= n_full)
+            off = lane < tail ? beta_lane : 0u;
+        return gload_u16(base_beta + int64_t(x) * beta_chunk_bytes + off);
+    }
+    // sigmoid(beta) of chunk x into its ring slot, 0 on rows past the end.
+    __device__ void put_beta(int x, uint32_t logit) const
+    {
+        const int len = x < n_full ? C : tail;
+        const float b = sigmoid_f32(bf16_to_f32(static_cast<uint16_t>(logit)));
+        if (lane < C)
+            lds_st(st_beta + static_cast<uint32_t>(x % 3) * kTileBeta, lane < len ? b : 0.f);
+    }
 
     // -A of chunk x: lane (j = l16, g4) gets (Kt Kh^T)[4 g4 + e][j].
     __device__ void a_stage(int x) const
     {
-        const int s2 = x & 1, s3 = x % 3, s4 = x & 3;
+        const uint32_t s2 = x & 1, s3 = x % 3, s4 = x & 3;
+        const uint32_t ak = slot_base(tok + s4 * kTile + kOffKt), ah = slot_base(tok + s2 * kTile + kOffKh);
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
-            acc = mfma32(tok_operand32(sh.kt_col[s4], kt, l16, g4),
-                         tok_operand32(sh.kh_col[s2], kt, l16, g4), acc);
-        const f32x4_t b = lds_load<f32x4_t>(&sh.beta[s3][4 * g4]);
+            acc = mfma32(lds_tr32(ak + 64 * C * kt), lds_tr32(ah + 64 * C * kt), acc);
+        const f32x4_t b = lds_ld<f32x4_t>(bt + s3 * kTileBeta);
+        const uint32_t am = slot_base(amat_st + s2 * kTileA);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = 4 * g4 + e;
-            sh.amat[s2][i][l16] = l16 < i ? -b[e] * acc[e] : 0.f;  // stored negated
+            lds_st(am + 4 * AP * e, l16 < i ? -b[e] * acc[e] : 0.f);  // stored negated
         }
     }
 
@@ -379,23 +470,23 @@ struct SolveWave {
     // P[i][4 g4 .. 4 g4 + 3], the layout the state stage reads.
     __device__ void p_stage(int x) const
     {
-        const int s2 = x & 1, s4 = x & 3, s5 = x % 5;
+        const uint32_t s2 = x & 1, s4 = x & 3, s5 = x % 5;
+        const uint32_t ah = slot_base(tok + s2 * kTile + kOffKh), aq = slot_base(tok + s5 * kTile + kOffQt);
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
-            acc = mfma32(tok_operand32(sh.kh_col[s2], kt, l16, g4),
-                         tok_operand32(sh.qt_col[s5], kt, l16, g4), acc);
+            acc = mfma32(lds_tr32(ah + 64 * C * kt), lds_tr32(aq + 64 * C * kt), acc);
         f32x4_t pm;
 #pragma unroll
         for (int e = 0; e < 4; ++e) pm[e] = (4 * g4 + e <= l16) ? acc[e] : 0.f;
-        lds_store(&sh.pmat[s4][l16][chunk16(l16, g4)], pack_bf16x4(pm));
+        lds_st(r16 + s4 * kTileCC + kOffP, pack_bf16x4(pm));
     }
 
     // Columns 8 (pw - 2) .. 8 (pw - 2) + 7 of T for chunk x (solve waves 2
     // and 3), stored as T diag(beta).
     __device__ void solve_stage(int x) const
     {
-        const int s2 = x & 1, s3 = x % 3;
+        const uint32_t s2 = x & 1, s3 = x % 3;
         // T[:, j] for j = j0, j0 + 1 with j0 = 8 (pw - 2) + 2 g4; lane
         // (g4, l16 = row i).  Right-looking forward substitution on
         // v = e_j - A t: lane i starts from v_i = (i == j); step m takes
@@ -404,10 +495,11 @@ struct SolveWave {
         // v_i.  A[i][m] = 0 for m >= i, so a row stops changing once it is
         // final.  The two columns run as independent chains.
         const int j0 = 8 * (pw - 2) + 2 * g4, i = l16;
+        const uint32_t ar = slot_base(amat_ld + s2 * kTileA);
         float nrow[C];  // -A[i][:], zero from column i on
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-            const f32x4_t v = lds_load<f32x4_t>(&sh.amat[s2][i][4 * q4]);
+            const f32x4_t v = lds_ld<f32x4_t>(ar + 16 * q4);
             nrow[4 * q4 + 0] = v[0];
             nrow[4 * q4 + 1] = v[1];
             nrow[4 * q4 + 2] = v[2];
@@ -415,16 +507,15 @@ struct SolveWave {
         }
         float v0 = i == j0 ? 1.0f : 0.0f, v1 = i == j0 + 1 ? 1.0f : 0.0f;
         solve_steps(nrow, v0, v1);
-        const f32x2_t b2 = lds_load<f32x2_t>(&sh.beta[s3][j0]);
+        const f32x2_t b2 = lds_ld<f32x2_t>(bt + s3 * kTileBeta);
         const float tb0 = v0 * b2[0];
         const float tb1 = v1 * b2[1];
         const __bf16 hi0 = static_cast<__bf16>(tb0), hi1 = static_cast<__bf16>(tb1);
         const __bf16 lo0 = static_cast<__bf16>(tb0 - static_cast<float>(hi0));
         const __bf16 lo1 = static_cast<__bf16>(tb1 - static_cast<float>(hi1));
-        // elements (i, j0), (i, j0 + 1): chunk j0 / 4, positions j0 % 4, + 1
-        const int pos = chunk16(i, j0 >> 2) + (j0 & 3);
-        lds_store(&sh.tb_hi[s2][i][pos], pack_bf16x2(static_cast<float>(hi0), static_cast<float>(hi1)));
-        lds_store(&sh.tb_lo[s2][i][pos], pack_bf16x2(static_cast<float>(lo0), static_cast<float>(lo1)));
+        const uint32_t at = slot_base(tb_st + s2 * kTileCC);
+        lds_st(at + kOffThi, pack_bf16x2(static_cast<float>(hi0), static_cast<float>(hi1)));
+        lds_st(at + kOffTlo, pack_bf16x2(static_cast<float>(lo0), static_cast<float>(lo1)));
     }
 
     // One multiply-add per step and column, with t_m read straight from lane
@@ -450,24 +541,26 @@ struct SolveWave {
     // as the contraction [T_hi | T_lo] against [X; X].
     __device__ void wy_stage(int x) const
     {
-        const int s2 = x & 1, s4 = x & 3;
+        const uint32_t s2 = x & 1, s4 = x & 3, s6 = x % 6;
         const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
         // lane (l16, g4) holds (T diag(beta))[l16][4*g4 .. 4*g4+3]: the A
         // operand of T diag(beta) V and the B operand of Kt^T (T diag(beta))^T
-        const u32x2_t th = lds_load<u32x2_t>(&sh.tb_hi[s2][l16][chunk16(l16, g4)]);
-        const u32x2_t tl = lds_load<u32x2_t>(&sh.tb_lo[s2][l16][chunk16(l16, g4)]);
-        const bf16x8_t t8 = cat8(th, tl);
+        const uint32_t at = slot_base(r16 + s2 * kTileCC);
+        const bf16x8_t t8 = cat8(lds_ld<u32x2_t>(at + kOffThi), lds_ld<u32x2_t>(at + kOffTlo));
+        const uint32_t ak = slot_base(wy_k + s4 * kTile), aw = slot_base(wy_w + s2 * kTileW),
+                       au = slot_base(wy_u + s2 * kTileU);
+        const uint32_t av[2] = {slot_base(wy_v0 + s6 * kTile), slot_base(wy_v1 + s6 * kTile)};
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const int ch = 32 * pw + 16 * t + l16;
-            const u32x2_t ka = lds_load<u32x2_t>(&sh.kt_col[s4][ch][chunk16(ch, g4)]);
-            // lane (token l16, g4): W[l16][32pw+16t+4g4+i]
+            const u32x2_t ka = lds_ld<u32x2_t>(ak + 32 * C * t);
+            // lane (token l16, g4): W[l16][32pw+16t+4g4+i], stored at chunk
+            // 4 pw + g4, half t of the padded row
             const f32x4_t w = mfma32(cat8(ka, ka), t8, zero);
-            lds_store(&sh.w_row[s2][l16][tok_off(l16, 32 * pw + 16 * t + 4 * g4)], pack_bf16x4(w));
-            const u32x2_t vb = chan_operand(sh.v_row[s4], 32 * pw + 16 * t, l16, g4);
+            lds_st(aw + 8 * t, pack_bf16x4(w));
+            const u32x2_t vb = lds_tr(av[t]);
             // lane (vcol, g4): U~[4g4+i][vcol]
             const f32x4_t u = mfma32(t8, cat8(vb, vb), zero);
-            lds_store(&sh.ut[s2][ch][chunk32(ch, g4)], u);
+            lds_st(au + 64 * C * t, u);
         }
     }
 };
@@ -479,11 +572,16 @@ struct SolveWave {
 template <int INIT, int FINAL>
 struct StateWave {
     const FwdParams &p;
-    Shared &sh;
-    int64_t t_begin, t_end, chain;
+    int64_t chain;
     int w, lane, l16, g4;
-    uint16_t *dst_out;   // out at token t_begin, value column 32w + 4g4
-    int64_t tok_stride;  // H * 128
+    int n_full, tail;          // full chunks of the sequence; length of a partial last chunk
+    char *out_base;            // out at token t_begin, value column 32 w (wave-uniform)
+    int64_t out_chunk_bytes;   // between consecutive chunks of out: C * H * 256
+    uint32_t out_lane;         // lane offset: token l16, value column 4 g4
+    // LDS addresses (ring slot 0) of this lane's reads: Qt operands
+    // (tok_lane), W row l16 chunk g4, U~ column 32 w + l16, P row l16,
+    // Gamma_C rows 4 g4 .., Kbar channel l16.
+    uint32_t rd_q, rd_w, rd_u, rd_p, rd_g, rd_k;
     f32x4_t S[8][2];     // S[16mt + 4g4 + i][32w + 16nt + l16]
 
     __device__ int64_t state_index(int mt, int nt) const
@@ -533,24 +631,23 @@ struct StateWave {
 
     __device__ void chunk(int x)
     {
-        const int s2 = x & 1, s4 = x & 3, s5 = x % 5;
-        const int64_t left = t_end - (t_begin + int64_t(x) * C);
-        const int len = static_cast<int>(left < C ? left : C);
+        const uint32_t s2 = x & 1, s4 = x & 3, s5 = x % 5;
+        const int len = x < n_full ? C : tail;
 
         // X = W S (lane (vcol, g4): rows 4g4..4g4+3) and Y^T = S^T Qt^T (lane
         // (token, g4): value columns 4g4..4g4+3 of the tile), from the same
         // operand registers with the roles of A and B swapped.  S enters as
         // bf16 B operands: contraction slot 8*g4 + e maps to state row
         // 32kt + 4g4 + e (e < 4) and 32kt + 16 + 4g4 + (e - 4) (e >= 4), which
-        // is exactly what this lane's accumulators of tiles 2kt, 2kt+1 hold.
+        // is exactly what this lane's accumulators of tiles 2kt, 2kt+1 hold
+        // and what chunk 4 kt + g4 of a W row holds.
+        const uint32_t aw = slot_base(rd_w + s2 * kTileW), aq = slot_base(rd_q + s5 * kTile);
         f32x4_t X[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         f32x4_t Y[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
-            const int lo = tok_off(l16, 32 * kt + 4 * g4), hi = tok_off(l16, 32 * kt + 16 + 4 * g4);
-            const bf16x8_t wa = cat8(lds_load<u32x2_t>(&sh.w_row[s2][l16][lo]),
-                                     lds_load<u32x2_t>(&sh.w_row[s2][l16][hi]));
-            const bf16x8_t qa = tok_operand32(sh.qt_col[s5], kt, l16, g4);
+            const bf16x8_t wa = __builtin_bit_cast(bf16x8_t, lds_ld<u32x4_t>(aw + 64 * kt));
+            const bf16x8_t qa = lds_tr32(aq + 64 * C * kt);
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
                 const bf16x8_t sb = cat8(pack_bf16x4(S[2 * kt][nt]), pack_bf16x4(S[2 * kt + 1][nt]));
@@ -560,30 +657,28 @@ struct StateWave {
         }
 
         // U = U~ - W S, as bf16 operands (lane (vcol, g4): tokens 4g4..4g4+3)
+        const uint32_t au = slot_base(rd_u + s2 * kTileU);
         u32x2_t ub[2];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            const int vc = 32 * w + 16 * nt + l16;
-            const f32x4_t u = lds_load<f32x4_t>(&sh.ut[s2][vc][chunk32(vc, g4)]) - X[nt];
-            ub[nt] = pack_bf16x4(u);
-        }
-        const u32x2_t pa = lds_load<u32x2_t>(&sh.pmat[s4][l16][chunk16(l16, g4)]);
+        for (int nt = 0; nt < 2; ++nt) ub[nt] = pack_bf16x4(lds_ld<f32x4_t>(au + 64 * C * nt) - X[nt]);
+        const u32x2_t pa = lds_ld<u32x2_t>(slot_base(rd_p + s4 * kTileCC));
 
         // O^T = Y^T + U^T P^T; lane (token l16, g4) then holds 4 consecutive
         // output values of its token and stores them directly
+        char *const oc = out_base + int64_t(x) * out_chunk_bytes;
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
             const f32x4_t o = mfma16(ub[nt], pa, Y[nt]);
             if (l16 < len)
-                *reinterpret_cast<u32x2_t *>(dst_out + (int64_t(x) * C + l16) * tok_stride + 16 * nt) =
-                    pack_bf16x4(o);
+                *reinterpret_cast<u32x2_t *>(oc + out_lane + 32 * nt) = pack_bf16x4(o);
         }
 
         // S <- diag(Gamma_C) S + Kbar^T U
+        const uint32_t ag = slot_base(rd_g + s5 * kTileGam), ak = slot_base(rd_k + s5 * kTile);
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
-            const f32x4_t gc = lds_load<f32x4_t>(&sh.gam_c[s5][16 * mt + 4 * g4]);
-            const u32x2_t ka = lds_load<u32x2_t>(&sh.kb_col[s5][16 * mt + l16][chunk16(l16, g4)]);
+            const f32x4_t gc = lds_ld<f32x4_t>(ag + 64 * mt);
+            const u32x2_t ka = lds_ld<u32x2_t>(ak + 32 * C * mt);
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) S[mt][nt] = mfma16(ka, ub[nt], S[mt][nt] * gc);
         }
@@ -598,21 +693,36 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
     const int64_t n = chain / p.H, h = chain % p.H;
     int64_t t_begin, t_end, row;
     chain_segment(p, n, &t_begin, &t_end, &row);
-    const int64_t nchunks = (t_end - t_begin + C - 1) / C;  // < 2^31 (T is bounded on the host)
-    const int nc = static_cast<int>(nchunks);
+    // T < 2^31 and H <= 2^16 are checked on the host: the token counts below
+    // fit in int, the lane offsets of the loads and stores in 32 bits.
+    const int len_seq = static_cast<int>(t_end - t_begin);
+    const int n_full = len_seq / C, tail = len_seq % C;
+    const int nc = n_full + (tail > 0);
     // even, so that the gate waves' two-set loop needs no exit in between
     const int n_iter = nc > 0 ? (nc + kStages + 1) & ~1 : 0;
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int l16 = lane & 15, g4 = lane >> 4;
-    const int64_t tok_stride = p.H * D;
+    const int64_t tok_bytes = p.H * D * 2;                  // between consecutive tokens
     const int64_t first = (row * p.T + t_begin) * p.H + h;  // token-head row of t_begin
+    const uint32_t sh0 = lds_addr(&sh);
 
     if (wave < 4) {
-        StateWave<INIT, FINAL> sw{p, sh, t_begin, t_end, chain, wave, lane, l16, g4,
-                                  p.out + first * D + 32 * wave + 4 * g4, tok_stride, {}};
+        StateWave<INIT, FINAL> sw{p, chain, wave, lane, l16, g4, n_full, tail,
+                                  reinterpret_cast<char *>(p.out + first * D + 32 * wave),
+                                  C * tok_bytes,
+                                  static_cast<uint32_t>(l16 * tok_bytes + 8 * g4),
+                                  sh0 + kOffQt + tok_lane(l16, g4),
+                                  sh0 + kOffW + 2 * kWPitch * l16 + 16 * g4,
+                                  sh0 + kOffU + 128 * C * wave + row32_lane(l16, g4),
+                                  sh0 + kOffP + row16_lane(l16, g4),
+                                  sh0 + kOffGam + 16 * g4,
+                                  sh0 + kOffKb + row16_lane(l16, g4),
+                                  {}};
         __builtin_amdgcn_s_setprio(3);
         sw.load_state();
+        if (n_iter > 0)
+            lds_barrier();  // the gate waves' first loads are in LDS
         for (int it = 0; it < n_iter; ++it) {
             if (it >= kStages && it - kStages < nc)
                 sw.chunk(it - kStages);
@@ -624,16 +734,60 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
 
     if (wave >= 12) {
         const int pw = wave - 12;
-        const SolveWave sv{sh, pw, l16, g4};
+        const int j0 = 8 * (pw - 2) + 2 * g4;  // the solve waves' column pair
+        const SolveWave sv{pw, l16, g4,
+                           sh0 + tok_lane(l16, g4),
+                           sh0 + row16_lane(l16, g4),
+                           sh0 + kOffA + 4 * (4 * g4 * AP + l16),
+                           sh0 + kOffA + 4 * AP * l16,
+                           sh0 + kOffBeta + (pw == 0 ? 16 * g4 : 4 * j0),
+                           sh0 + 2 * (l16 * C + chunk16(l16, j0 >> 2) + (j0 & 3)),
+                           sh0 + kOffKt + 64 * C * pw + row16_lane(l16, g4),
+                           sh0 + kOffW + 2 * kWPitch * l16 + 16 * (4 * pw + g4),
+                           sh0 + kOffV + chan_lane(32 * pw, l16, g4),
+                           sh0 + kOffV + chan_lane(32 * pw + 16, l16, g4),
+                           sh0 + kOffU + 128 * C * pw + row32_lane(l16, g4),
+                           lane, n_full, tail,
+                           reinterpret_cast<const char *>(p.beta + first),
+                           C * p.H * 2,
+                           lane < C ? static_cast<uint32_t>(lane * p.H * 2) : 0u,
+                           sh0 + kOffBeta + 4 * lane};
         __builtin_amdgcn_s_setprio(3);
-        for (int it = 0; it < n_iter; ++it) {
-            if (pw < 2) {
-                if (it >= 1 && it - 1 < nc) {
-                    if (pw == 0)
-                        sv.a_stage(it - 1);
-                    else
-                        sv.p_stage(it - 1);
+        if (pw == 0) {
+            // A of chunk it - 1 and WY of chunk it - 3 each iteration; the beta
+            // logits of chunk y are loaded at iteration y - 1 into register
+            // set y % 2 and used at iteration y + 1, where they first go to
+            // LDS for the solve of chunk y at iteration y + 2.
+            uint32_t b_even = nc > 0 ? sv.load_beta(0) : 0u, b_odd = 0;  // no chunk: nothing to read
+            if (n_iter > 0)
+                lds_barrier();  // the gate waves' first loads are in LDS
+            for (int it = 0; it < n_iter; it += 2) {
+                if (it >= 1 && it - 1 < nc) {  // chunk it - 1 (odd)
+                    sv.put_beta(it - 1, b_odd);
+                    sv.a_stage(it - 1);
                 }
+                b_odd = sv.load_beta(it + 1 < nc ? it + 1 : nc - 1);
+                if (it >= 3 && it - 3 < nc)
+                    sv.wy_stage(it - 3);
+                lds_barrier();
+                if (it < nc) {  // chunk it (even)
+                    sv.put_beta(it, b_even);
+                    sv.a_stage(it);
+                }
+                b_even = sv.load_beta(it + 2 < nc ? it + 2 : nc - 1);
+                if (it >= 2 && it - 2 < nc)
+                    sv.wy_stage(it - 2);
+                lds_barrier();
+            }
+            wait_vmem<0>();  // no load may still be writing registers when the wave ends
+            return;
+        }
+        if (n_iter > 0)
+            lds_barrier();  // the gate waves' first loads are in LDS
+        for (int it = 0; it < n_iter; ++it) {
+            if (pw == 1) {
+                if (it >= 1 && it - 1 < nc)
+                    sv.p_stage(it - 1);
             } else if (it >= 2 && it - 2 < nc)
                 sv.solve_stage(it - 2);
             if (it >= 3 && it - 3 < nc)
@@ -644,52 +798,52 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
     }
 
     // gate waves
-    const int gc16 = wave - 4;
-    const int64_t wave_off = (first * D + 16 * gc16) * 2;  // bytes
-    const int64_t tok_bytes = tok_stride * 2;
-    GateWave gw{p, sh, t_begin, t_end, gc16, lane, l16, g4,
-                reinterpret_cast<const char *>(p.q) + wave_off,
-                reinterpret_cast<const char *>(p.k) + wave_off,
-                reinterpret_cast<const char *>(p.g) + wave_off,
-                reinterpret_cast<const char *>(p.v) + wave_off,
-                reinterpret_cast<const char *>(p.beta + first),
-                C * tok_bytes, C * p.H * 2,
-                l16 * tok_bytes + 8 * g4, 8 * g4, lane * p.H * 2};
+    const int gc16 = wave - 4, tens = gc16 >> 1, hf = gc16 & 1;
+    const uint16_t *const src = tens == 0 ? p.q : tens == 1 ? p.k : tens == 2 ? p.g : p.v;
+    uint32_t dma_full[2], dma_tail[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int r = 8 * hf + 4 * j + (lane >> 4), c = (lane & 15) ^ r;
+        dma_full[j] = static_cast<uint32_t>(r * tok_bytes + 16 * c);
+        dma_tail[j] = static_cast<uint32_t>((r < tail ? r : 0) * tok_bytes + 16 * c);
+    }
+    GateWave gw{p, gc16, lane, l16, g4, n_full, tail,
+                reinterpret_cast<const char *>(src + first * D),
+                C * tok_bytes,
+                {dma_full[0], dma_full[1]}, {dma_tail[0], dma_tail[1]},
+                sh0 + (tens < 3 ? kOffStage + tens * kTile : kOffV) + 2 * D * 8 * hf,
+                tens < 3 ? 3 * kTile : kTile,
+                tens < 3 ? 3 : 6,
+                sh0 + kOffStage + chan_lane(16 * gc16, l16, g4),
+                sh0 + 512 * gc16 + row16_lane(l16, g4),
+                sh0 + kOffGam + 4 * (16 * gc16 + l16)};
     const float head_mult = p.A_log ? expf(p.A_log[h]) : 1.0f;
     gw.head_neg = -head_mult * kLog2eF;
     gw.bias_neg = p.dt_bias ? gw.head_neg * p.dt_bias[h * D + 16 * gc16 + l16] : 0.f;
-    {
-        uint16_t idb[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) idb[e] = (4 * g4 + e == l16) ? 0x3F80 : 0;
-        gw.ident = u32x2_t{uint32_t(idb[0]) | (uint32_t(idb[1]) << 16),
-                           uint32_t(idb[2]) | (uint32_t(idb[3]) << 16)};
-    }
     gw.grp_hi = g4 >= 2 ? 1.0f : 0.0f;
     gw.grp_odd = (g4 & 1) ? 1.0f : 0.0f;
     if (n_iter == 0)
         return;
 
-    // Two register sets alternate: iteration `it` uses the set holding chunk
-    // it (loaded two iterations earlier), runs the gate stage on it and
-    // reloads the set with chunk it + 2.  Past the last chunk the stage runs
+    // The stage ring holds three chunks: iteration `it` runs the gate stage on
+    // chunk it, starts the loads of chunk it + 2 and, before the barrier,
+    // waits for those of chunk it + 1 (issued one iteration earlier), so every
+    // chunk has two iterations to arrive.  Past the last chunk the stage runs
     // on a repeat of it and fills only ring slots that no later stage reads.
     // The state and solve waves (priority 3) sit on the critical path; the
     // gate waves fill the issue slots they leave.
     __builtin_amdgcn_s_setprio(1);
-    RawRegs ra{}, rb{};
-    gw.issue(ra, 0);
-    asm volatile("" ::: "memory");  // keep the two sets' loads in order
-    gw.issue(rb, nc > 1 ? 1 : 0);
-    for (int it = 0; it < n_iter; it += 2) {
-        gw.gate_stage(it, ra);
-        gw.issue(ra, it + 2 < nc ? it + 2 : nc - 1);
-        lds_barrier();
-        gw.gate_stage(it + 1, rb);
-        gw.issue(rb, it + 3 < nc ? it + 3 : nc - 1);
+    gw.issue(0);
+    gw.issue(nc > 1 ? 1 : 0);
+    wait_vmem<kLoadsPerChunk>();
+    lds_barrier();
+    for (int it = 0; it < n_iter; ++it) {
+        gw.gate_stage(it);
+        gw.issue(it + 2 < nc ? it + 2 : nc - 1);
+        wait_vmem<kLoadsPerChunk>();
         lds_barrier();
     }
-    // no load may still be writing registers when the wave ends
+    // no load may still be writing LDS when the wave ends
     wait_vmem<0>();
 }
 

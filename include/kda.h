@@ -56,9 +56,9 @@ typedef enum kda_status {
                                   final_state both given with different dtypes */
     KDA_ERR_ALIAS = 6,         /* out or final_state overlaps an input, or
                                   final_state partly overlaps initial_state */
-    KDA_ERR_SIZE = 7,          /* B < 1, H < 1, T < 0 or T > 2^31-1, sizes
-                                  overflow int64, or more than 2^31-1
-                                  (sequence, head) chains */
+    KDA_ERR_SIZE = 7,          /* B < 1, H < 1, H > 65536, T < 0 or
+                                  T > 2^31-1, sizes overflow int64, or more
+                                  than 2^31-1 (sequence, head) chains */
     KDA_ERR_SCALE = 8,         /* scale is not finite */
     KDA_ERR_LAUNCH = 9         /* the HIP runtime rejected the launch */
 } kda_status;

@@ -94,6 +94,7 @@ def call(**over):
     (dict(init=ADDR[8], init_dtype=2, final=ADDR[8] + 4, final_dtype=2), _lib.KDA_ERR_ALIAS),
     (dict(B=0), _lib.KDA_ERR_SIZE),
     (dict(H=0), _lib.KDA_ERR_SIZE),
+    (dict(H=65537), _lib.KDA_ERR_SIZE),
     (dict(T=-1), _lib.KDA_ERR_SIZE),
     (dict(B=1 << 40, T=1 << 30), _lib.KDA_ERR_SIZE),
     (dict(scale=math.inf), _lib.KDA_ERR_SCALE),
