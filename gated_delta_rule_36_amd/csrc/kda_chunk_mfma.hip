@@ -762,19 +762,19 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
             if (n_iter > 0)
                 lds_barrier();  // the gate waves' first loads are in LDS
             for (int it = 0; it < n_iter; it += 2) {
-                if (it >= 1 && it - 1 < nc) {  // chunk it - 1 (odd)
+                if (it >= 1 && it - 1 < nc)  // chunk it - 1 (odd)
                     sv.put_beta(it - 1, b_odd);
-                    sv.a_stage(it - 1);
-                }
                 b_odd = sv.load_beta(it + 1 < nc ? it + 1 : nc - 1);
+                if (it >= 1 && it - 1 < nc)
+                    sv.a_stage(it - 1);
                 if (it >= 3 && it - 3 < nc)
                     sv.wy_stage(it - 3);
                 lds_barrier();
-                if (it < nc) {  // chunk it (even)
+                if (it < nc)  // chunk it (even)
                     sv.put_beta(it, b_even);
-                    sv.a_stage(it);
-                }
                 b_even = sv.load_beta(it + 2 < nc ? it + 2 : nc - 1);
+                if (it < nc)
+                    sv.a_stage(it);
                 if (it >= 2 && it - 2 < nc)
                     sv.wy_stage(it - 2);
                 lds_barrier();
@@ -825,10 +825,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
     if (n_iter == 0)
         return;
 
-    // The stage ring holds three chunks: iteration `it` runs the gate stage on
-    // chunk it, starts the loads of chunk it + 2 and, before the barrier,
-    // waits for those of chunk it + 1 (issued one iteration earlier), so every
-    // chunk has two iterations to arrive.  Past the last chunk the stage runs
+    // The stage ring holds three chunks: iteration `it` starts the loads of
+    // chunk it + 2, runs the gate stage on chunk it and, before the barrier,
+    // waits for the loads of chunk it + 1 (issued one iteration earlier), so
+    // every chunk has two iterations to arrive.  Past the last chunk the stage runs
     // on a repeat of it and fills only ring slots that no later stage reads.
     // The state and solve waves (priority 3) sit on the critical path; the
     // gate waves fill the issue slots they leave.
@@ -838,8 +838,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
     wait_vmem<kLoadsPerChunk>();
     lds_barrier();
     for (int it = 0; it < n_iter; ++it) {
-        gw.gate_stage(it);
+        // slot of chunk it + 2 (stage: last read by the gate stage of chunk
+        // it - 1; V: by WY of chunk it - 4, both before the last barrier)
         gw.issue(it + 2 < nc ? it + 2 : nc - 1);
+        gw.gate_stage(it);
         wait_vmem<kLoadsPerChunk>();
         lds_barrier();
     }
