@@ -577,7 +577,7 @@ struct StateWave {
     int n_full, tail;          // full chunks of the sequence; length of a partial last chunk
     char *out_base;            // out at token t_begin, value column 32 w (wave-uniform)
     int64_t out_chunk_bytes;   // between consecutive chunks of out: C * H * 256
-    uint32_t out_lane;         // lane offset: token l16, value column 4 g4
+    uint32_t out_lane;         // lane offset: token l16, value column 8 g4
     // LDS addresses (ring slot 0) of this lane's reads: Qt operands
     // (tok_lane), W row l16 chunk g4, U~ column 32 w + l16, P row l16,
     // Gamma_C rows 4 g4 .., Kbar channel l16.
@@ -665,13 +665,18 @@ struct StateWave {
 
         // O^T = Y^T + U^T P^T; lane (token l16, g4) then holds 4 consecutive
         // output values of its token and stores them directly
-        char *const oc = out_base + int64_t(x) * out_chunk_bytes;
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            const f32x4_t o = mfma16(ub[nt], pa, Y[nt]);
-            if (l16 < len)
-                *reinterpret_cast<u32x2_t *>(oc + out_lane + 32 * nt) = pack_bf16x4(o);
-        }
+        const u32x2_t o0 = pack_bf16x4(mfma16(ub[0], pa, Y[0]));
+        const u32x2_t o1 = pack_bf16x4(mfma16(ub[1], pa, Y[1]));
+        // regroup across the 16-lane rows so that lane (l16, g4) holds value
+        // columns 8 g4 .. 8 g4 + 7 of its token: one 16-byte store per lane
+        uint32_t a0 = o0[0], a1 = o0[1], b0 = o1[0], b1 = o1[1];
+        swap_rows32(a0, b0);
+        swap_rows32(a1, b1);
+        swap_rows16(a0, b0);
+        swap_rows16(a1, b1);
+        if (l16 < len)
+            *reinterpret_cast<u32x4_t *>(out_base + int64_t(x) * out_chunk_bytes + out_lane) =
+                u32x4_t{a0, a1, b0, b1};
 
         // S <- diag(Gamma_C) S + Kbar^T U
         const uint32_t ag = slot_base(rd_g + s5 * kTileGam), ak = slot_base(rd_k + s5 * kTile);
@@ -711,7 +716,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
         StateWave<INIT, FINAL> sw{p, chain, wave, lane, l16, g4, n_full, tail,
                                   reinterpret_cast<char *>(p.out + first * D + 32 * wave),
                                   C * tok_bytes,
-                                  static_cast<uint32_t>(l16 * tok_bytes + 8 * g4),
+                                  static_cast<uint32_t>(l16 * tok_bytes + 16 * g4),
                                   sh0 + kOffQt + tok_lane(l16, g4),
                                   sh0 + kOffW + 2 * kWPitch * l16 + 16 * g4,
                                   sh0 + kOffU + 128 * C * wave + row32_lane(l16, g4),

@@ -133,7 +133,7 @@ def make_inputs(B: int, T: int, H: int, *, lower_bound: float, seed: int = 0,
                      final_dtype=final_dtype)
 
 
-# The five named workloads (seed 0 each).
+# The named workloads (seed 0 each).
 WORKLOADS = {
     "tiny_b1_t64_h2": dict(B=1, T=64, H=2, lower_bound=-5.0),
     "small_b2_t128_h8": dict(B=2, T=128, H=8, lower_bound=-5.0),
@@ -143,9 +143,17 @@ WORKLOADS = {
                                     init_dtype=torch.bfloat16, final_dtype=torch.bfloat16),
     "large_b8_t16384_h32": dict(B=8, T=16384, H=32, lower_bound=-5.0,
                                 final_dtype=torch.float32),
+    # decode-shaped calls: a few new tokens per sequence, the fp32 state
+    # carried in and out (the state traffic dominates)
+    "decode_b64_t1_h32_state": dict(B=64, T=1, H=32, lower_bound=-5.0,
+                                    init_dtype=torch.float32, final_dtype=torch.float32),
+    "decode_b64_t8_h32_state": dict(B=64, T=8, H=32, lower_bound=-5.0,
+                                    init_dtype=torch.float32, final_dtype=torch.float32),
+    "decode_b64_t15_h32_state": dict(B=64, T=15, H=32, lower_bound=-5.0,
+                                     init_dtype=torch.float32, final_dtype=torch.float32),
 }
 
 
 def workload(name: str, seed: int = 0, device: str = "cpu") -> KdaInputs:
-    """Draw one of the five named workloads on ``device``."""
+    """Draw one of the named workloads on ``device``."""
     return make_inputs(**WORKLOADS[name], seed=seed, device=device)

@@ -98,11 +98,12 @@ def check_full(tag, x, final_dtype):
 
 
 # --------------------------------------------------------------------------
-# the five named workloads
+# the named workloads
 # --------------------------------------------------------------------------
 
 @pytest.mark.parametrize("name", ["tiny_b1_t64_h2", "small_b2_t128_h8",
-                                  "long_b1_t8192_h16_state"])
+                                  "long_b1_t8192_h16_state", "decode_b64_t1_h32_state",
+                                  "decode_b64_t8_h32_state", "decode_b64_t15_h32_state"])
 def test_workload_parity_full(name):
     print(f"[case] workload {name}", flush=True)
     x = synth.workload(name, device="cuda")
