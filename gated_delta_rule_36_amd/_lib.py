@@ -7,8 +7,9 @@ import os
 LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
 # Every symbol include/kda.h declares.
-EXPORTS = ("kda_fwd", "kda_status_string", "kda_abi_version")
-ABI_VERSION = 1
+EXPORTS = ("kda_fwd", "kda_fwd_scan", "kda_fwd_scan_workspace_bytes", "kda_status_string",
+           "kda_abi_version")
+ABI_VERSION = 2
 
 # kda_status codes (include/kda.h)
 KDA_OK = 0
@@ -21,6 +22,7 @@ KDA_ERR_ALIAS = 6
 KDA_ERR_SIZE = 7
 KDA_ERR_SCALE = 8
 KDA_ERR_LAUNCH = 9
+KDA_ERR_WORKSPACE = 10
 
 # kda_dtype codes
 KDA_DTYPE_NONE = 0
@@ -48,6 +50,11 @@ def load() -> ctypes.CDLL:
     lib.kda_fwd.argtypes = [p, p, p, p, p, d, p, p, p, d, p, ctypes.c_int, p, ctypes.c_int,
                             p, i64, i64, i64, i64, i64, i64, p]
     lib.kda_fwd.restype = ctypes.c_int
+    lib.kda_fwd_scan.argtypes = [p, p, p, p, p, d, p, p, p, d, p, ctypes.c_int, p, ctypes.c_int,
+                                 p, i64, i64, i64, i64, i64, i64, i64, p, i64, p]
+    lib.kda_fwd_scan.restype = ctypes.c_int
+    lib.kda_fwd_scan_workspace_bytes.argtypes = [p, i64, i64, i64, i64, i64]
+    lib.kda_fwd_scan_workspace_bytes.restype = i64
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_abi_version.argtypes = []

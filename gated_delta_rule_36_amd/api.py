@@ -12,7 +12,7 @@ and ``dt_bias [H,128]``, ``lower_bound`` in [-5, 0], optional bf16/fp32
 """
 from __future__ import annotations
 
-from typing import Optional
+from typing import Optional, Union
 
 import torch
 
@@ -58,13 +58,21 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
         lower_bound: float, initial_state: Optional[torch.Tensor] = None,
         final_state: Optional[torch.Tensor] = None,
         cu_seqlens: Optional[torch.Tensor] = None, *,
-        check_cu_seqlens: bool = True) -> torch.Tensor:
+        check_cu_seqlens: bool = True,
+        segment_chunks: Union[None, int, str] = None) -> torch.Tensor:
     """Run the chunked KDA forward pass; writes ``out`` (and ``final_state``).
 
     Enqueued on the current stream of ``q``'s device; returns ``out``.
     ``check_cu_seqlens`` copies ``cu_seqlens`` to the host (a synchronising
     copy) to check it is nondecreasing from 0 to T; the kernels never read
     outside the tensors either way.
+
+    ``segment_chunks`` selects the segmented form (``kda_fwd_scan``: each
+    sequence cut into segments of that many 16-token chunks, processed in
+    parallel and stitched by an fp32 combine step) for workloads with few
+    (sequence, head) chains; ``"auto"`` picks a segment length from the
+    sizes (:func:`auto_segment_chunks`), ``None`` runs ``kda_fwd``.  The
+    workspace is a temporary allocation on the same stream.
     """
     if not isinstance(q, torch.Tensor):
         raise TypeError("q must be a torch.Tensor")
@@ -127,16 +135,48 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
             raise ValueError(f"{name} must be [N,H,V,K] = {(N, H, V, K)}, got {tuple(st.shape)}")
         codes.append(_STATE_CODES[st.dtype])
 
+    if segment_chunks == "auto":
+        segment_chunks = auto_segment_chunks(N * H, T)
+    elif segment_chunks is not None and (not isinstance(segment_chunks, int)
+                                         or isinstance(segment_chunks, bool) or segment_chunks < 1):
+        raise ValueError(f"segment_chunks must be a positive int, 'auto' or None, got {segment_chunks!r}")
+
     lib = _lib.load()
     with torch.cuda.device(device):
         stream = torch.cuda.current_stream(device).cuda_stream
-        status = lib.kda_fwd(
-            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(out),
-            _ptr(A_log), _ptr(dt_bias), float(lower_bound),
-            _ptr(initial_state), codes[0], _ptr(final_state), codes[1],
-            _ptr(cu_seqlens), num_seqs, B, T, H, K, V, stream)
+        args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(out),
+                _ptr(A_log), _ptr(dt_bias), float(lower_bound),
+                _ptr(initial_state), codes[0], _ptr(final_state), codes[1],
+                _ptr(cu_seqlens), num_seqs, B, T, H, K, V)
+        if segment_chunks is None:
+            status = lib.kda_fwd(*args, stream)
+        else:
+            nbytes = lib.kda_fwd_scan_workspace_bytes(_ptr(cu_seqlens), num_seqs, B, T, H,
+                                                      segment_chunks)
+            if nbytes < 0:
+                raise ValueError("bad sizes for the segmented form")
+            # freed right after the call: the caching allocator hands it out
+            # again only to work ordered after this call on the same stream
+            workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+            status = lib.kda_fwd_scan(*args, segment_chunks, workspace.data_ptr(), nbytes, stream)
     if status != _lib.KDA_OK:
         if status == _lib.KDA_ERR_LAUNCH:
             raise KdaError(status)
         raise KdaArgumentError(status)
     return out
+
+
+def auto_segment_chunks(chains: int, T: int, target_blocks: int = 256,
+                        min_chunks: int = 8, min_segments: int = 6) -> Optional[int]:
+    """Segment length (in 16-token chunks) for the segmented form, or None
+    when it would not help.  With ``chains`` (sequence, head) chains of at
+    most ``T`` tokens, each chain is cut into about ``target_blocks / chains``
+    segments (one workgroup per CU on a 256-CU part) of at least
+    ``min_chunks`` chunks.  The segmented form walks every segment about
+    three times (end state, transition matrix, output) against once for a
+    whole chain, so it needs ``min_segments`` segments or more to pay off."""
+    chunks = -(-T // 16)
+    if chains <= 0 or target_blocks // chains < min_segments:
+        return None
+    seg = max(min_chunks, -(-chunks // (target_blocks // chains)))
+    return None if -(-chunks // seg) < min_segments else seg

@@ -34,15 +34,21 @@ Span span(const void *p, int64_t bytes)
 
 bool valid_kind(kda_dtype d) { return d == KDA_DTYPE_BF16 || d == KDA_DTYPE_FP32; }
 
-}  // namespace
+// Validated arguments of a forward call, and the byte ranges the alias
+// checks need.
+struct Checked {
+    kda::FwdParams p;
+    int64_t chains = 0;
+    Span spans[11];  // inputs, out, final_state, initial_state
+    int n_spans = 0;
+};
 
-extern "C" kda_status kda_fwd(const void *q, const void *k, const void *v, const void *g,
-                              const void *beta, double scale, void *out, const float *A_log,
-                              const float *dt_bias, double lower_bound,
-                              const void *initial_state, kda_dtype initial_state_dtype,
-                              void *final_state, kda_dtype final_state_dtype,
-                              const int64_t *cu_seqlens, int64_t num_seqs, int64_t B,
-                              int64_t T, int64_t H, int64_t K, int64_t V, void *stream)
+kda_status check_args(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                      double scale, void *out, const float *A_log, const float *dt_bias,
+                      double lower_bound, const void *initial_state, kda_dtype initial_state_dtype,
+                      void *final_state, kda_dtype final_state_dtype, const int64_t *cu_seqlens,
+                      int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+                      Checked *c)
 {
     if (K != kda::kHeadDim || V != kda::kHeadDim)
         return KDA_ERR_HEAD_DIM;
@@ -93,11 +99,12 @@ extern "C" kda_status kda_fwd(const void *q, const void *k, const void *v, const
         return KDA_ERR_ALIAS;
     if (sf.overlaps(si) && final_state != initial_state)
         return KDA_ERR_ALIAS;
+    for (const Span &s : inputs) c->spans[c->n_spans++] = s;
+    c->spans[c->n_spans++] = so;
+    c->spans[c->n_spans++] = sf;
+    c->spans[c->n_spans++] = si;
 
-    if (chains == 0)
-        return KDA_OK;
-
-    kda::FwdParams p;
+    kda::FwdParams &p = c->p;
     p.q = static_cast<const uint16_t *>(q);
     p.k = static_cast<const uint16_t *>(k);
     p.v = static_cast<const uint16_t *>(v);
@@ -118,8 +125,94 @@ extern "C" kda_status kda_fwd(const void *q, const void *k, const void *v, const
     // The gate is carried in log2 units so that every decay is a plain exp2
     // (lower_bound page, "Conversion to the Gate Scale Factor").
     p.gate_scale = static_cast<float>(lower_bound * kLog2e);
+    c->chains = chains;
+    return KDA_OK;
+}
 
-    hipError_t err = kda::launch_forward(p, static_cast<hipStream_t>(stream));
+// Segments per chain for segments of seg_chunks chunks: every sequence has
+// at most T tokens.  -1 if seg_chunks < 1.
+int64_t segments_per_chain(int64_t T, int64_t seg_chunks)
+{
+    if (seg_chunks < 1)
+        return -1;
+    const int64_t chunks = (T + kda::kChunk - 1) / kda::kChunk;
+    return chunks > 0 ? (chunks + seg_chunks - 1) / seg_chunks : 1;
+}
+
+constexpr int64_t kSlabBytes = int64_t(kda::kHeadDim) * kda::kHeadDim * 4;  // one fp32 state
+
+}  // namespace
+
+extern "C" kda_status kda_fwd(const void *q, const void *k, const void *v, const void *g,
+                              const void *beta, double scale, void *out, const float *A_log,
+                              const float *dt_bias, double lower_bound,
+                              const void *initial_state, kda_dtype initial_state_dtype,
+                              void *final_state, kda_dtype final_state_dtype,
+                              const int64_t *cu_seqlens, int64_t num_seqs, int64_t B,
+                              int64_t T, int64_t H, int64_t K, int64_t V, void *stream)
+{
+    Checked c;
+    const kda_status st = check_args(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
+                                     initial_state, initial_state_dtype, final_state,
+                                     final_state_dtype, cu_seqlens, num_seqs, B, T, H, K, V, &c);
+    if (st != KDA_OK)
+        return st;
+    if (c.chains == 0)
+        return KDA_OK;
+    hipError_t err = kda::launch_forward(c.p, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+extern "C" int64_t kda_fwd_scan_workspace_bytes(const int64_t *cu_seqlens, int64_t num_seqs,
+                                                int64_t B, int64_t T, int64_t H,
+                                                int64_t seg_chunks)
+{
+    const int64_t n_seg = segments_per_chain(T, seg_chunks);
+    const int64_t N = cu_seqlens ? num_seqs : B;
+    int64_t chains, slabs, bytes;
+    if (n_seg < 0 || N < 0 || H < 1 || T < 0 || !mul_ok(N, H, &chains) ||
+        !mul_ok(chains, n_seg, &slabs) || !mul_ok(slabs, 2 * kSlabBytes, &bytes))
+        return -1;
+    return bytes;
+}
+
+extern "C" kda_status kda_fwd_scan(const void *q, const void *k, const void *v, const void *g,
+                                   const void *beta, double scale, void *out, const float *A_log,
+                                   const float *dt_bias, double lower_bound,
+                                   const void *initial_state, kda_dtype initial_state_dtype,
+                                   void *final_state, kda_dtype final_state_dtype,
+                                   const int64_t *cu_seqlens, int64_t num_seqs, int64_t B,
+                                   int64_t T, int64_t H, int64_t K, int64_t V, int64_t seg_chunks,
+                                   void *workspace, int64_t workspace_bytes, void *stream)
+{
+    Checked c;
+    const kda_status st = check_args(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
+                                     initial_state, initial_state_dtype, final_state,
+                                     final_state_dtype, cu_seqlens, num_seqs, B, T, H, K, V, &c);
+    if (st != KDA_OK)
+        return st;
+    const int64_t n_seg = segments_per_chain(T, seg_chunks);
+    int64_t blocks;
+    // grids: chains * n_seg blocks for the map and output passes
+    if (n_seg < 0 || !mul_ok(c.chains, n_seg, &blocks) || blocks > INT32_MAX)
+        return KDA_ERR_SIZE;
+    const int64_t need = blocks * 2 * kSlabBytes;
+    if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+        return KDA_ERR_WORKSPACE;
+    const Span sw = span(workspace, need);
+    for (int i = 0; i < c.n_spans; ++i) {
+        if (sw.overlaps(c.spans[i]))
+            return KDA_ERR_WORKSPACE;
+    }
+    if (c.chains == 0)
+        return KDA_OK;
+    kda::FwdParams &p = c.p;
+    p.seg_chunks = seg_chunks;
+    p.n_seg = n_seg;
+    p.seg_b = static_cast<float *>(workspace);
+    p.seg_m = p.seg_b + blocks * (kSlabBytes / 4);
+    hipError_t err = n_seg == 1 ? kda::launch_chunk_mfma(p, static_cast<hipStream_t>(stream))
+                                : kda::launch_forward_scan(p, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
@@ -136,6 +229,7 @@ extern "C" const char *kda_status_string(kda_status status)
     case KDA_ERR_SIZE: return "bad size (B >= 1, 1 <= H <= 65536, 0 <= T < 2^31, no int64 overflow)";
     case KDA_ERR_SCALE: return "scale must be finite";
     case KDA_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
+    case KDA_ERR_WORKSPACE: return "workspace is NULL, not 16-byte aligned, too small, or overlaps a tensor";
     }
     return "unknown status";
 }
@@ -152,5 +246,25 @@ hipError_t launch_forward(const FwdParams &p, hipStream_t stream)
         return e && std::strcmp(e, "simt") == 0;
     }();
     return use_simt ? launch_chunk_simt(p, stream) : launch_chunk_mfma(p, stream);
+}
+
+// The segmented form: map (end states, then transition matrices), combine,
+// output; four launches in order on one stream.
+hipError_t launch_forward_scan(const FwdParams &p, hipStream_t stream)
+{
+    FwdParams s = p;
+    s.phase = kPhaseMapB;
+    hipError_t err = launch_chunk_mfma(s, stream);
+    if (err == hipSuccess && p.n_seg > 2) {
+        s.phase = kPhaseMapM;
+        err = launch_chunk_mfma(s, stream);
+        if (err == hipSuccess)
+            err = launch_scan_combine(s, stream);
+    }
+    if (err == hipSuccess) {
+        s.phase = kPhaseOut;
+        err = launch_chunk_mfma(s, stream);
+    }
+    return err;
 }
 }  // namespace kda

@@ -569,13 +569,16 @@ struct SolveWave {
 // state waves
 // ---------------------------------------------------------------------------
 
-template <int INIT, int FINAL>
+// Where a state wave's state comes from and goes to (wave-uniform).
+enum StateSrc : int { kSrcZero = 0, kSrcIdentity = 1, kSrcFp32 = 2, kSrcBf16 = 3 };
+enum ChunkMode : int { kChunkFull = 0, kChunkState = 1, kChunkTransition = 2 };
+enum StateDst : int { kDstNone = 0, kDstFp32 = 2, kDstBf16 = 3 };
+
 struct StateWave {
     const FwdParams &p;
-    int64_t chain;
     int w, lane, l16, g4;
-    int n_full, tail;          // full chunks of the sequence; length of a partial last chunk
-    char *out_base;            // out at token t_begin, value column 32 w (wave-uniform)
+    int n_full, tail;          // full chunks of the range; length of a partial last chunk
+    char *out_base;            // out at the range's first token, value column 32 w (wave-uniform)
     int64_t out_chunk_bytes;   // between consecutive chunks of out: C * H * 256
     uint32_t out_lane;         // lane offset: token l16, value column 8 g4
     // LDS addresses (ring slot 0) of this lane's reads: Qt operands
@@ -584,43 +587,48 @@ struct StateWave {
     uint32_t rd_q, rd_w, rd_u, rd_p, rd_g, rd_k;
     f32x4_t S[8][2];     // S[16mt + 4g4 + i][32w + 16nt + l16]
 
-    __device__ int64_t state_index(int mt, int nt) const
+    // Element offset, within one [V][K] state slab, of this lane's tile (mt, nt).
+    __device__ int64_t slab_index(int mt, int nt) const
     {
-        return (chain * D + 32 * w + 16 * nt + l16) * D + 16 * mt + 4 * g4;
+        return int64_t(32 * w + 16 * nt + l16) * D + 16 * mt + 4 * g4;
     }
 
-    __device__ void load_state()
+    // slab: element offset of the [V][K] slab in ptr.
+    __device__ void load_state(int src, const void *ptr, int64_t slab)
     {
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
-                const int64_t idx = state_index(mt, nt);
-                if constexpr (INIT == kStateFp32) {
-                    S[mt][nt] = *reinterpret_cast<const f32x4_t *>(
-                        static_cast<const float *>(p.init_state) + idx);
-                } else if constexpr (INIT == kStateBf16) {
-                    const u32x2_t b = *reinterpret_cast<const u32x2_t *>(
-                        static_cast<const uint16_t *>(p.init_state) + idx);
+                const int64_t idx = slab + slab_index(mt, nt);
+                if (src == kSrcFp32) {
+                    S[mt][nt] = *reinterpret_cast<const f32x4_t *>(static_cast<const float *>(ptr) + idx);
+                } else if (src == kSrcBf16) {
+                    const u32x2_t b = *reinterpret_cast<const u32x2_t *>(static_cast<const uint16_t *>(ptr) + idx);
                     S[mt][nt] = f32x4_t{__uint_as_float(b[0] << 16), __uint_as_float(b[0] & 0xffff0000u),
                                         __uint_as_float(b[1] << 16), __uint_as_float(b[1] & 0xffff0000u)};
                 } else {
-                    S[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                    const int v = 32 * w + 16 * nt + l16;  // identity: S[k][v] = (k == v)
+                    const float one = src == kSrcIdentity ? 1.0f : 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) S[mt][nt][i] = (16 * mt + 4 * g4 + i == v) ? one : 0.0f;
                 }
             }
     }
 
-    __device__ void store_state() const
+    __device__ void store_state(int dst, void *ptr, int64_t slab) const
     {
+        if (dst == kDstNone)
+            return;
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
-                const int64_t idx = state_index(mt, nt);
-                if constexpr (FINAL == kStateFp32) {
-                    *reinterpret_cast<f32x4_t *>(static_cast<float *>(p.final_state) + idx) = S[mt][nt];
-                } else if constexpr (FINAL == kStateBf16) {
-                    *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(p.final_state) + idx) =
+                const int64_t idx = slab + slab_index(mt, nt);
+                if (dst == kDstFp32) {
+                    *reinterpret_cast<f32x4_t *>(static_cast<float *>(ptr) + idx) = S[mt][nt];
+                } else {
+                    *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(ptr) + idx) =
                         u32x2_t{uint32_t(f32_to_bf16_rne(S[mt][nt][0])) |
                                     (uint32_t(f32_to_bf16_rne(S[mt][nt][1])) << 16),
                                 uint32_t(f32_to_bf16_rne(S[mt][nt][2])) |
@@ -629,8 +637,13 @@ struct StateWave {
             }
     }
 
+    // MODE kChunkFull: outputs and state; kChunkState: the state only (no
+    // Y, no output); kChunkTransition: the state with v ignored (U = -W S),
+    // which carries an identity start to the range's transition matrix.
+    template <int MODE>
     __device__ void chunk(int x)
     {
+        constexpr bool kOut = MODE == kChunkFull;
         const uint32_t s2 = x & 1, s4 = x & 3, s5 = x % 5;
         const int len = x < n_full ? C : tail;
 
@@ -652,31 +665,39 @@ struct StateWave {
             for (int nt = 0; nt < 2; ++nt) {
                 const bf16x8_t sb = cat8(pack_bf16x4(S[2 * kt][nt]), pack_bf16x4(S[2 * kt + 1][nt]));
                 X[nt] = mfma32(wa, sb, X[nt]);
-                Y[nt] = mfma32(sb, qa, Y[nt]);
+                if constexpr (kOut)
+                    Y[nt] = mfma32(sb, qa, Y[nt]);
             }
         }
 
         // U = U~ - W S, as bf16 operands (lane (vcol, g4): tokens 4g4..4g4+3)
-        const uint32_t au = slot_base(rd_u + s2 * kTileU);
         u32x2_t ub[2];
+        if constexpr (MODE == kChunkTransition) {
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) ub[nt] = pack_bf16x4(lds_ld<f32x4_t>(au + 64 * C * nt) - X[nt]);
-        const u32x2_t pa = lds_ld<u32x2_t>(slot_base(rd_p + s4 * kTileCC));
+            for (int nt = 0; nt < 2; ++nt) ub[nt] = pack_bf16x4(-X[nt]);
+        } else {
+            const uint32_t au = slot_base(rd_u + s2 * kTileU);
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) ub[nt] = pack_bf16x4(lds_ld<f32x4_t>(au + 64 * C * nt) - X[nt]);
+        }
 
-        // O^T = Y^T + U^T P^T; lane (token l16, g4) then holds 4 consecutive
-        // output values of its token and stores them directly
-        const u32x2_t o0 = pack_bf16x4(mfma16(ub[0], pa, Y[0]));
-        const u32x2_t o1 = pack_bf16x4(mfma16(ub[1], pa, Y[1]));
-        // regroup across the 16-lane rows so that lane (l16, g4) holds value
-        // columns 8 g4 .. 8 g4 + 7 of its token: one 16-byte store per lane
-        uint32_t a0 = o0[0], a1 = o0[1], b0 = o1[0], b1 = o1[1];
-        swap_rows32(a0, b0);
-        swap_rows32(a1, b1);
-        swap_rows16(a0, b0);
-        swap_rows16(a1, b1);
-        if (l16 < len)
-            *reinterpret_cast<u32x4_t *>(out_base + int64_t(x) * out_chunk_bytes + out_lane) =
-                u32x4_t{a0, a1, b0, b1};
+        if constexpr (kOut) {
+            // O^T = Y^T + U^T P^T; lane (token l16, g4) then holds 4
+            // consecutive output values of its token
+            const u32x2_t pa = lds_ld<u32x2_t>(slot_base(rd_p + s4 * kTileCC));
+            const u32x2_t o0 = pack_bf16x4(mfma16(ub[0], pa, Y[0]));
+            const u32x2_t o1 = pack_bf16x4(mfma16(ub[1], pa, Y[1]));
+            // regroup across the 16-lane rows so that lane (l16, g4) holds
+            // value columns 8 g4 .. 8 g4 + 7 of its token: one 16-byte store
+            uint32_t a0 = o0[0], a1 = o0[1], b0 = o1[0], b1 = o1[1];
+            swap_rows32(a0, b0);
+            swap_rows32(a1, b1);
+            swap_rows16(a0, b0);
+            swap_rows16(a1, b1);
+            if (l16 < len)
+                *reinterpret_cast<u32x4_t *>(out_base + int64_t(x) * out_chunk_bytes + out_lane) =
+                    u32x4_t{a0, a1, b0, b1};
+        }
 
         // S <- diag(Gamma_C) S + Kbar^T U
         const uint32_t ag = slot_base(rd_g + s5 * kTileGam), ak = slot_base(rd_k + s5 * kTile);
@@ -690,16 +711,87 @@ struct StateWave {
     }
 };
 
-template <int INIT, int FINAL>
+template <int MODE>
+__device__ __forceinline__ void state_loop(StateWave &sw, int n_iter, int nc)
+{
+    for (int it = 0; it < n_iter; ++it) {
+        if (it >= kStages && it - kStages < nc)
+            sw.chunk<MODE>(it - kStages);
+        lds_barrier();
+    }
+}
+
+// MODE: the state waves' chunk mode (kChunkFull for whole chains and the
+// output pass, kChunkState for the segment end states, kChunkTransition for
+// the segment transition matrices).  One mode per kernel: with several state
+// loops in one kernel the compiler runs out of registers.
+template <int MODE>
 __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
 {
     __shared__ Shared sh;
-    const int64_t chain = blockIdx.x;
-    const int64_t n = chain / p.H, h = chain % p.H;
+    // Block -> chain (and, in the segmented form, segment).  The grid is
+    // below 2^31 blocks (checked on the host), so 32-bit arithmetic suffices;
+    // readfirstlane keeps these wave-uniform values in scalar registers.
+    const int n_seg = static_cast<int>(p.n_seg);
+    int chain = blockIdx.x, seg = 0;
+    if (p.phase != kPhaseWhole) {
+        chain = static_cast<int>(blockIdx.x) / n_seg;
+        seg = static_cast<int>(blockIdx.x) - chain * n_seg;
+    }
+    chain = __builtin_amdgcn_readfirstlane(chain);
+    seg = __builtin_amdgcn_readfirstlane(seg);
+    const int H = static_cast<int>(p.H);
+    const int64_t n = chain / H, h = chain - (chain / H) * H;
     int64_t t_begin, t_end, row;
     chain_segment(p, n, &t_begin, &t_end, &row);
-    // T < 2^31 and H <= 2^16 are checked on the host: the token counts below
-    // fit in int, the lane offsets of the loads and stores in 32 bits.
+
+    // Where this block's state starts and ends, and its token range (all
+    // wave-uniform).
+    int src = p.init_state ? (p.init_kind == kStateBf16 ? kSrcBf16 : kSrcFp32) : kSrcZero;
+    const void *src_ptr = p.init_state;
+    int64_t src_slab = int64_t(chain) * D * D;
+    int dst = p.final_state ? (p.final_kind == kStateBf16 ? kDstBf16 : kDstFp32) : kDstNone;
+    void *dst_ptr = p.final_state;
+    int64_t dst_slab = int64_t(chain) * D * D;
+    if (p.phase != kPhaseWhole) {
+        const int64_t nc_chain = (t_end - t_begin + C - 1) / C;
+        const int segs = static_cast<int>(nc_chain > 0 ? (nc_chain + p.seg_chunks - 1) / p.seg_chunks : 1);
+        const int64_t scratch = (int64_t(chain) * n_seg + seg) * D * D;
+        if (p.phase == kPhaseMapB) {
+            // b_s for segments 0 .. segs - 2: segment 0 from the real start,
+            // later ones from zero
+            if (seg >= segs - 1)
+                return;
+            if (seg > 0)
+                src = kSrcZero;
+            dst = kDstFp32;
+            dst_ptr = p.seg_b;
+            dst_slab = scratch;
+        } else if (p.phase == kPhaseMapM) {
+            // M_s for segments 1 .. segs - 2 (segment 0 starts from a known state)
+            if (seg == 0 || seg >= segs - 1)
+                return;
+            src = kSrcIdentity;
+            dst = kDstFp32;
+            dst_ptr = p.seg_m;
+            dst_slab = scratch;
+        } else {
+            // outputs of every segment from its true start state: the real
+            // one for segment 0, seg_b[s - 1] (after the combine step) for
+            // the others; the chain's last segment writes the final state
+            if (seg >= segs)
+                return;
+            if (seg > 0) {
+                src = kSrcFp32;
+                src_ptr = p.seg_b;
+                src_slab = scratch - D * D;
+            }
+            if (seg != segs - 1)
+                dst = kDstNone;
+        }
+        t_begin += int64_t(seg) * p.seg_chunks * C;
+        t_end = t_end < t_begin + p.seg_chunks * C ? t_end : t_begin + p.seg_chunks * C;
+    }
     const int len_seq = static_cast<int>(t_end - t_begin);
     const int n_full = len_seq / C, tail = len_seq % C;
     const int nc = n_full + (tail > 0);
@@ -713,7 +805,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
     const uint32_t sh0 = lds_addr(&sh);
 
     if (wave < 4) {
-        StateWave<INIT, FINAL> sw{p, chain, wave, lane, l16, g4, n_full, tail,
+        StateWave sw{p, wave, lane, l16, g4, n_full, tail,
                                   reinterpret_cast<char *>(p.out + first * D + 32 * wave),
                                   C * tok_bytes,
                                   static_cast<uint32_t>(l16 * tok_bytes + 16 * g4),
@@ -725,15 +817,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
                                   sh0 + kOffKb + row16_lane(l16, g4),
                                   {}};
         __builtin_amdgcn_s_setprio(3);
-        sw.load_state();
+        sw.load_state(src, src_ptr, src_slab);
         if (n_iter > 0)
             lds_barrier();  // the gate waves' first loads are in LDS
-        for (int it = 0; it < n_iter; ++it) {
-            if (it >= kStages && it - kStages < nc)
-                sw.chunk(it - kStages);
-            lds_barrier();
-        }
-        sw.store_state();
+        state_loop<MODE>(sw, n_iter, nc);
+        sw.store_state(dst, dst_ptr, dst_slab);
         return;
     }
 
@@ -804,7 +892,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
 
     // gate waves
     const int gc16 = wave - 4, tens = gc16 >> 1, hf = gc16 & 1;
-    const uint16_t *const src = tens == 0 ? p.q : tens == 1 ? p.k : tens == 2 ? p.g : p.v;
+    const uint16_t *const tensor = tens == 0 ? p.q : tens == 1 ? p.k : tens == 2 ? p.g : p.v;
     uint32_t dma_full[2], dma_tail[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -813,7 +901,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
         dma_tail[j] = static_cast<uint32_t>((r < tail ? r : 0) * tok_bytes + 16 * c);
     }
     GateWave gw{p, gc16, lane, l16, g4, n_full, tail,
-                reinterpret_cast<const char *>(src + first * D),
+                reinterpret_cast<const char *>(tensor + first * D),
                 C * tok_bytes,
                 {dma_full[0], dma_full[1]}, {dma_tail[0], dma_tail[1]},
                 sh0 + (tens < 3 ? kOffStage + tens * kTile : kOffV) + 2 * D * 8 * hf,
@@ -854,35 +942,18 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
     wait_vmem<0>();
 }
 
-template <int INIT, int FINAL>
-hipError_t launch(const FwdParams &p, hipStream_t stream)
-{
-    const int64_t chains = p.num_seqs * p.H;
-    FwdParams args = p;
-    void *argv[] = {&args};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&chunk_mfma_kernel<INIT, FINAL>),
-                           dim3(static_cast<unsigned>(chains)), dim3(kThreads), argv, 0, stream);
-}
-
-template <int INIT>
-hipError_t launch_final(const FwdParams &p, hipStream_t stream)
-{
-    switch (p.final_kind) {
-    case kStateBf16: return launch<INIT, kStateBf16>(p, stream);
-    case kStateFp32: return launch<INIT, kStateFp32>(p, stream);
-    default: return launch<INIT, kStateNone>(p, stream);
-    }
-}
-
 }  // namespace
 
 hipError_t launch_chunk_mfma(const FwdParams &p, hipStream_t stream)
 {
-    switch (p.init_kind) {
-    case kStateBf16: return launch_final<kStateBf16>(p, stream);
-    case kStateFp32: return launch_final<kStateFp32>(p, stream);
-    default: return launch_final<kStateNone>(p, stream);
-    }
+    const int64_t chains = p.num_seqs * p.H;
+    const int64_t blocks = p.phase == kPhaseWhole ? chains : chains * p.n_seg;
+    const void *kernel = p.phase == kPhaseMapB   ? reinterpret_cast<const void *>(&chunk_mfma_kernel<kChunkState>)
+                         : p.phase == kPhaseMapM ? reinterpret_cast<const void *>(&chunk_mfma_kernel<kChunkTransition>)
+                                                 : reinterpret_cast<const void *>(&chunk_mfma_kernel<kChunkFull>);
+    FwdParams args = p;
+    void *argv[] = {&args};
+    return hipLaunchKernel(kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), argv, 0, stream);
 }
 
 }  // namespace kda

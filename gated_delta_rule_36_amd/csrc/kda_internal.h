@@ -11,6 +11,7 @@ constexpr int kChunk = 16;     // tokens per chunk (fixed, as on the chunk-size 
 constexpr int kHeadDim = 128;  // K = V = 128
 
 enum StateKind : int { kStateNone = 0, kStateBf16 = 1, kStateFp32 = 2 };
+enum Phase : int { kPhaseWhole = 0, kPhaseMapB = 1, kPhaseMapM = 2, kPhaseOut = 3 };
 
 // Everything a launch needs.  Pointers are device pointers; sizes were
 // validated by the front end.
@@ -27,13 +28,35 @@ struct FwdParams {
     int64_t T, H;                          // token axis length, heads
     float scale;                           // read-out scale
     float gate_scale;                      // lower_bound * log2(e), in fp32
+
+    // Intra-sequence scan (kda_fwd_scan).  Every chain is cut into segments
+    // of seg_chunks chunks; segment s maps its start state S to M_s S + b_s
+    // (the recurrence is affine in the state).  Phases: kPhaseWhole (whole
+    // chains, kda_fwd); kPhaseMapB: b_s of segments 0 .. last-1 into seg_b
+    // (segment 0 from the real initial state, the others from zero);
+    // kPhaseMapM: M_s of segments 1 .. last-1 into seg_m (identity start, v
+    // ignored); then the combine step turns seg_b[s] into the true start
+    // state of segment s + 1; kPhaseOut: every segment from its true start
+    // state, writing outputs, and the final state from the last segment.
+    int phase = 0;
+    int64_t seg_chunks = 0;  // chunks per segment (phase != kPhaseWhole)
+    int64_t n_seg = 1;       // segments per chain, the longest chain's count
+    float *seg_b = nullptr;  // fp32 [chains][n_seg][V][K]
+    float *seg_m = nullptr;  // fp32 [chains][n_seg][V][K]
 };
 
 // Enqueue the whole forward pass on `stream`.  Returns the launch status.
 hipError_t launch_forward(const FwdParams &p, hipStream_t stream);
 
+// Enqueue the segmented form: map (phase 1), combine, output (phase 3).
+// p.seg_chunks, p.n_seg, p.seg_b and p.seg_m must be set.
+hipError_t launch_forward_scan(const FwdParams &p, hipStream_t stream);
+
 // Individual kernel launchers (one per implementation).
 hipError_t launch_chunk_mfma(const FwdParams &p, hipStream_t stream);
 hipError_t launch_chunk_simt(const FwdParams &p, hipStream_t stream);
+// The combine step of the segmented form: for every chain and s >= 1,
+// seg_b[c][s] <- M_s seg_b[c][s-1] + seg_b[c][s] (in stored [V][K] terms).
+hipError_t launch_scan_combine(const FwdParams &p, hipStream_t stream);
 
 }  // namespace kda

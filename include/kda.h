@@ -60,7 +60,11 @@ typedef enum kda_status {
                                   T > 2^31-1, sizes overflow int64, or more
                                   than 2^31-1 (sequence, head) chains */
     KDA_ERR_SCALE = 8,         /* scale is not finite */
-    KDA_ERR_LAUNCH = 9         /* the HIP runtime rejected the launch */
+    KDA_ERR_LAUNCH = 9,        /* the HIP runtime rejected the launch */
+    KDA_ERR_WORKSPACE = 10     /* kda_fwd_scan: workspace NULL, not 16-byte
+                                  aligned, smaller than
+                                  kda_fwd_scan_workspace_bytes(), or
+                                  overlapping a tensor argument */
 } kda_status;
 
 /* Element type of initial_state / final_state. */
@@ -112,11 +116,62 @@ kda_status kda_fwd(const void *q, const void *k, const void *v, const void *g,
                    int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
                    void *stream);
 
+/*
+ * kda_fwd_scan - the same forward pass as kda_fwd (same arguments, same
+ * results up to rounding), computed with parallelism inside each sequence:
+ * for workloads with few (sequence, head) chains, where kda_fwd leaves most
+ * of the GPU idle.
+ *
+ * Each chain is cut into segments of seg_chunks chunks (16 tokens each).
+ * The recurrence above is affine in the state, so a segment maps its start
+ * state S to M S + b.  The call enqueues four steps on `stream`: b for every
+ * segment but the last (segment 0 from the real initial state, the others
+ * from zero), M for the inner segments (the state update with v set to zero,
+ * from an identity start), a combine step that walks each chain's segments
+ * in order (start of segment s+1 = M_s * start of s + b_s, in fp32), and the
+ * output pass, every segment from its true start state.  M and b stay fp32,
+ * so the results match kda_fwd's to within the rounding of the bf16 matrix
+ * operands both forms use.
+ *
+ *   seg_chunks       chunks per segment, >= 1 (KDA_ERR_SIZE otherwise).  One
+ *                    segment per chain (seg_chunks >= ceil(T / 16)) is exactly
+ *                    kda_fwd.
+ *   workspace        DEVICE scratch owned by the caller, 16-byte aligned, at
+ *                    least kda_fwd_scan_workspace_bytes() bytes, not
+ *                    overlapping any tensor argument.  Its contents on entry
+ *                    are ignored and on return are unspecified; it must not be
+ *                    used by other work until the call's work has completed
+ *                    on `stream`.
+ *   workspace_bytes  its size in bytes.
+ * Every other argument, the ownership rules and the error codes are those of
+ * kda_fwd, plus KDA_ERR_WORKSPACE.  The segmented form always runs on the
+ * MFMA kernels.
+ */
+kda_status kda_fwd_scan(const void *q, const void *k, const void *v, const void *g,
+                        const void *beta, double scale, void *out,
+                        const float *A_log, const float *dt_bias, double lower_bound,
+                        const void *initial_state, kda_dtype initial_state_dtype,
+                        void *final_state, kda_dtype final_state_dtype,
+                        const int64_t *cu_seqlens, int64_t num_seqs,
+                        int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+                        int64_t seg_chunks, void *workspace, int64_t workspace_bytes,
+                        void *stream);
+
+/*
+ * Bytes of workspace kda_fwd_scan needs for these sizes: two fp32 128x128
+ * slabs per (chain, segment), with ceil(ceil(T/16) / seg_chunks) segments per
+ * chain (every sequence has at most T tokens).  cu_seqlens is only tested for
+ * NULL (batch mode: N = B chains per head) and never read.  Returns -1 for
+ * seg_chunks < 1, negative sizes or overflow.
+ */
+int64_t kda_fwd_scan_workspace_bytes(const int64_t *cu_seqlens, int64_t num_seqs,
+                                     int64_t B, int64_t T, int64_t H, int64_t seg_chunks);
+
 /* Static, NUL-terminated description of a status code. */
 const char *kda_status_string(kda_status status);
 
 /* ABI version of this header (bumped on any signature change). */
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 int kda_abi_version(void);
 
 #ifdef __cplusplus

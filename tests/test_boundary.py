@@ -105,9 +105,77 @@ def test_argument_errors_are_reported_before_launch(over, code):
 
 
 def test_status_strings_are_distinct():
-    msgs = [_lib.status_string(c) for c in range(10)]
-    assert len(set(msgs)) == 10 and msgs[0] == "ok"
+    msgs = [_lib.status_string(c) for c in range(11)]
+    assert len(set(msgs)) == 11 and msgs[0] == "ok"
     assert _lib.status_string(123) == "unknown status"
+
+
+# --------------------------------------------------------------------------
+# kda_fwd_scan: workspace size and its argument errors (host checks only)
+# --------------------------------------------------------------------------
+
+SLAB = 128 * 128 * 4
+
+
+def test_scan_workspace_bytes():
+    ws = _lib.load().kda_fwd_scan_workspace_bytes
+    # 16 chains of 512 chunks in segments of 32: 16 segments, two fp32 slabs each
+    assert ws(None, 0, 1, 8192, 16, 32) == 16 * 16 * 2 * SLAB
+    # a partial last segment still counts, and T = 0 has one (empty) segment
+    assert ws(None, 0, 2, 8192 + 1, 3, 32) == 6 * 17 * 2 * SLAB
+    assert ws(None, 0, 2, 0, 3, 5) == 6 * 1 * 2 * SLAB
+    # packed mode counts num_seqs chains per head; cu_seqlens is not read
+    assert ws(ADDR[9], 5, 1, 100, 2, 1) == 10 * 7 * 2 * SLAB
+    assert ws(None, 0, 1, 64, 1, 0) == -1
+    assert ws(None, 0, 1, -1, 1, 4) == -1
+    assert ws(None, 0, 1 << 40, 1 << 30, 1 << 20, 1) == -1
+
+
+# separate 4 KiB dummies: with T = 1 the declared spans (256 bytes per token
+# tensor) stay inside them, so only the planted overlap is seen
+BIG = [ctypes.create_string_buffer(1 << 12) for _ in range(12)]
+BADDR = [ctypes.addressof(b) for b in BIG]
+
+
+def call_scan(seg=4, ws=None, ws_bytes=1 << 30, **over):
+    a = dict(q=BADDR[0], k=BADDR[1], v=BADDR[2], g=BADDR[3], beta=BADDR[4], scale=0.1,
+             out=BADDR[5], A_log=BADDR[6], dt_bias=BADDR[7], lower_bound=-5.0,
+             init=None, init_dtype=0, final=None, final_dtype=0, cu=None, num_seqs=0,
+             B=1, T=0, H=1, K=128, V=128)
+    a.update(over)
+    return _lib.load().kda_fwd_scan(a["q"], a["k"], a["v"], a["g"], a["beta"], a["scale"], a["out"],
+                                    a["A_log"], a["dt_bias"], a["lower_bound"], a["init"],
+                                    a["init_dtype"], a["final"], a["final_dtype"], a["cu"],
+                                    a["num_seqs"], a["B"], a["T"], a["H"], a["K"], a["V"],
+                                    seg, ws, ws_bytes, None)
+
+
+# Every call fails on the planted error, so nothing is launched.
+@pytest.mark.parametrize("kw,code", [
+    (dict(seg=0, ws=BADDR[11]), _lib.KDA_ERR_SIZE),
+    (dict(seg=-3, ws=BADDR[11]), _lib.KDA_ERR_SIZE),
+    (dict(ws=None), _lib.KDA_ERR_WORKSPACE),
+    (dict(ws=BADDR[11], ws_bytes=2 * SLAB - 1), _lib.KDA_ERR_WORKSPACE),
+    (dict(ws=BADDR[11] + 4), _lib.KDA_ERR_WORKSPACE),
+    (dict(ws=BADDR[0], T=1), _lib.KDA_ERR_WORKSPACE),          # overlaps q
+    (dict(ws=BADDR[5] - 64, T=1), _lib.KDA_ERR_WORKSPACE),     # overlaps out
+    (dict(ws=BADDR[11], K=64), _lib.KDA_ERR_HEAD_DIM),         # kda_fwd's checks come first
+    (dict(ws=BADDR[11], out=BADDR[0], T=1), _lib.KDA_ERR_ALIAS),
+])
+def test_scan_argument_errors_are_reported_before_launch(kw, code):
+    over = {k: v for k, v in kw.items() if k not in ("seg", "ws", "ws_bytes")}
+    args = {k: v for k, v in kw.items() if k in ("seg", "ws", "ws_bytes")}
+    assert call_scan(**args, **over) == code
+
+
+def test_auto_segment_chunks_policy():
+    auto = kda.auto_segment_chunks
+    assert auto(16, 8192) == 32          # 16 chains x 16 segments of 32 chunks
+    assert auto(1, 100000) == 25         # one chain: about 256 segments
+    assert auto(128, 1 << 20) is None    # enough chains already
+    assert auto(256, 16384) is None
+    assert auto(4, 200) is None          # too short to cut
+    assert auto(0, 1000) is None
 
 
 def test_empty_token_tensors_may_be_null():

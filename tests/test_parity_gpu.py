@@ -48,9 +48,11 @@ def _guards_intact(buf, dtype):
     return bool((buf[:GUARD] == s).all()) and bool((buf[-GUARD:] == s).all())
 
 
-def run_gpu(x: synth.KdaInputs, final_dtype=None, initial_state="inputs", out_fill=None):
+def run_gpu(x: synth.KdaInputs, final_dtype=None, initial_state="inputs", out_fill=None,
+            segment_chunks=None):
     """Run the library on inputs already on the GPU; returns (out, final) on
-    the CPU as float64 numpy arrays (final None if not requested)."""
+    the CPU as float64 numpy arrays (final None if not requested).
+    ``segment_chunks`` selects the segmented form (kda_fwd_scan)."""
     B, T, H, _ = x.q.shape
     N = x.num_seqs
     ob, out = _guarded((B, T, H, 128), torch.bfloat16)
@@ -61,7 +63,8 @@ def run_gpu(x: synth.KdaInputs, final_dtype=None, initial_state="inputs", out_fi
     if final_dtype is not None:
         fb, final = _guarded((N, H, 128, 128), final_dtype)
     kda.fwd(x.q, x.k, x.v, x.g, x.beta, x.scale, out, x.A_log, x.dt_bias, x.lower_bound,
-            initial_state=init, final_state=final, cu_seqlens=x.cu_seqlens)
+            initial_state=init, final_state=final, cu_seqlens=x.cu_seqlens,
+            segment_chunks=segment_chunks)
     torch.cuda.synchronize()
     assert _guards_intact(ob, torch.bfloat16), "write outside out"
     if fb is not None:
@@ -88,8 +91,8 @@ def assert_close(name, got, ref):
     assert mx <= MAX_ABS, f"{name}: max abs {mx:.3e} > {MAX_ABS}"
 
 
-def check_full(tag, x, final_dtype):
-    o, f = run_gpu(x, final_dtype)
+def check_full(tag, x, final_dtype, segment_chunks=None):
+    o, f = run_gpu(x, final_dtype, segment_chunks=segment_chunks)
     ro, rf = oracle_of(x)
     assert_close(f"{tag} out", o, ro)
     if final_dtype is not None:
@@ -317,3 +320,89 @@ def test_errors_raise_before_launch_on_gpu():
     with pytest.raises(ValueError):
         kda.fwd(x.q, x.k, x.v, x.g, x.beta, x.scale, out, x.A_log, x.dt_bias, -1.0,
                 cu_seqlens=torch.tensor([0, 5, 3, 16], device="cuda"))
+
+
+# --------------------------------------------------------------------------
+# the segmented form (kda_fwd_scan): parallel over segments of each chain
+# --------------------------------------------------------------------------
+
+def test_scan_long_workload_parity():
+    """16 chains of 512 chunks: the case the segmented form is for."""
+    name = "long_b1_t8192_h16_state"
+    print(f"[case] scan {name}", flush=True)
+    x = synth.workload(name, device="cuda")
+    seg = kda.auto_segment_chunks(x.num_seqs * x.q.shape[2], x.q.shape[1])
+    assert seg == 32
+    o, f = check_full(f"scan {name}", x, x.final_dtype, segment_chunks=seg)
+    # and it agrees with the whole-chain form as closely as either with the oracle
+    o1, f1 = run_gpu(x, x.final_dtype)
+    assert_close(f"scan vs whole {name} out", o, o1)
+    assert_close(f"scan vs whole {name} final", f, f1)
+
+
+@pytest.mark.parametrize("T,seg", [(17, 1), (100, 1), (100, 3), (257, 2), (257, 5), (48, 1)])
+def test_scan_ragged_lengths(T, seg):
+    print(f"[case] scan T={T} seg={seg}", flush=True)
+    x = synth.make_inputs(2, T, 3, lower_bound=-5.0, seed=100 + T + seg,
+                          init_dtype=torch.float32, device="cuda")
+    check_full(f"scan T={T} seg={seg}", x, torch.float32, segment_chunks=seg)
+
+
+@pytest.mark.parametrize("state,seg", [(torch.bfloat16, 1), (torch.float32, 2), (torch.bfloat16, 3)])
+def test_scan_varlen_edges(state, seg):
+    lens = [1, 16, 17, 0, 33, 5, 48, 2, 130]
+    print(f"[case] scan varlen {lens} state={state} seg={seg}", flush=True)
+    x = synth.make_inputs(1, 0, 4, lower_bound=-5.0, seed=21 + seg, seq_lengths=lens,
+                          init_dtype=state, device="cuda")
+    check_full(f"scan varlen {state} seg={seg}", x, state, segment_chunks=seg)
+
+
+def test_scan_states_absent_or_partial():
+    x = synth.make_inputs(1, 200, 2, lower_bound=-3.0, seed=31, device="cuda")
+    print("[case] scan no initial state", flush=True)
+    check_full("scan no init", x, torch.float32, segment_chunks=2)
+    print("[case] scan no final state", flush=True)
+    o, f = run_gpu(x, None, segment_chunks=2)
+    ro, _ = oracle_of(x)
+    assert f is None
+    assert_close("scan no final out", o, ro)
+
+
+def test_scan_in_place_state():
+    """final_state may be the initial_state buffer."""
+    print("[case] scan in-place state", flush=True)
+    x = synth.make_inputs(2, 150, 2, lower_bound=-5.0, seed=32, init_dtype=torch.float32,
+                          device="cuda")
+    ro, rf = oracle_of(x)
+    st = x.initial_state.clone()
+    out = torch.empty_like(x.v)
+    kda.fwd(x.q, x.k, x.v, x.g, x.beta, x.scale, out, x.A_log, x.dt_bias, x.lower_bound,
+            initial_state=st, final_state=st, segment_chunks=2)
+    torch.cuda.synchronize()
+    assert_close("scan in-place out", out.double().cpu().numpy(), ro)
+    assert_close("scan in-place final", st.double().cpu().numpy(), rf)
+
+
+def test_scan_one_segment_is_kda_fwd():
+    """A segment at least as long as every chain is the whole-chain kernel:
+    bit-identical results."""
+    print("[case] scan one segment", flush=True)
+    x = synth.make_inputs(2, 77, 3, lower_bound=-5.0, seed=33, init_dtype=torch.bfloat16,
+                          device="cuda")
+    o1, f1 = run_gpu(x, torch.bfloat16)
+    o2, f2 = run_gpu(x, torch.bfloat16, segment_chunks=5)
+    assert np.array_equal(o1, o2) and np.array_equal(f1, f2)
+
+
+def test_scan_max_decay_and_no_decay():
+    """The extremes of the transition matrices: every channel decaying by
+    the full e^lb per token, and no decay at all (lower_bound = 0)."""
+    x = synth.make_inputs(1, 160, 2, lower_bound=-5.0, seed=34, init_dtype=torch.float32,
+                          device="cuda")
+    x.g.fill_(100.0)
+    print("[case] scan max decay", flush=True)
+    check_full("scan max decay", x, torch.float32, segment_chunks=2)
+    y = synth.make_inputs(1, 160, 2, lower_bound=0.0, seed=35, init_dtype=torch.float32,
+                          device="cuda")
+    print("[case] scan no decay", flush=True)
+    check_full("scan no decay", y, torch.float32, segment_chunks=2)
