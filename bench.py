@@ -1,7 +1,9 @@
 """Benchmark of the KDA chunked forward pass on one MI355X.
 
-One step = one ``kda_fwd`` call over the whole workload (every stage of the
-forward pass runs inside it), inputs already resident in HBM.  The default
+One step = one forward call over the whole workload (every stage of the
+forward pass runs inside it), inputs already resident in HBM: ``kda_fwd``,
+or for workloads with few chains the segmented form ``kda_fwd_scan``
+(``--segment-chunks``; its four launches together make the step).  The default
 workload is the large throughput case: B=8, T=16384, H=32, K=V=128,
 lower_bound=-5, scale=1/sqrt(128), fp32 final_state written, no initial
 state.  Prints one JSON line:
@@ -14,6 +16,7 @@ state.  Prints one JSON line:
             the same workload (whole sequences of two batch rows)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--segment-chunks auto|off|N]
 """
 from __future__ import annotations
 
@@ -104,6 +107,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="large_b8_t16384_h32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--segment-chunks", default="auto",
+                    help="segmented form: 'auto' (used only for workloads with few chains), "
+                         "'off', or a segment length in 16-token chunks")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="before warm-up, run one plain device-to-device copy of this many "
                          "bytes (untimed), as a known-size reference for HBM byte counters")
@@ -135,10 +141,17 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    if args.segment_chunks == "auto":
+        seg = kda.auto_segment_chunks(x.num_seqs * H, T)
+    elif args.segment_chunks == "off":
+        seg = None
+    else:
+        seg = int(args.segment_chunks)
+
     def step():
         kda.fwd(x.q, x.k, x.v, x.g, x.beta, x.scale, out, x.A_log, x.dt_bias, x.lower_bound,
                 initial_state=x.initial_state, final_state=final, cu_seqlens=x.cu_seqlens,
-                check_cu_seqlens=False)
+                check_cu_seqlens=False, segment_chunks=seg)
 
     for _ in range(args.warmup):
         step()
@@ -186,7 +199,8 @@ def main():
         "config": {"workload": args.workload, "B": B, "T": T, "H": H, "K": K, "V": 128,
                    "lower_bound": x.lower_bound, "varlen": x.cu_seqlens is not None,
                    "initial_state": None if x.initial_state is None else str(x.initial_state.dtype),
-                   "final_state": None if final_dtype is None else str(final_dtype)},
+                   "final_state": None if final_dtype is None else str(final_dtype),
+                   "segment_chunks": seg},
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
