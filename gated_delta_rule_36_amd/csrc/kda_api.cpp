@@ -125,6 +125,7 @@ kda_status check_args(const void *q, const void *k, const void *v, const void *g
     // The gate is carried in log2 units so that every decay is a plain exp2
     // (lower_bound page, "Conversion to the Gate Scale Factor").
     p.gate_scale = static_cast<float>(lower_bound * kLog2e);
+    p.inverse = kda::inverse_from_env();
     c->chains = chains;
     return KDA_OK;
 }
@@ -246,6 +247,14 @@ hipError_t launch_forward(const FwdParams &p, hipStream_t stream)
         return e && std::strcmp(e, "simt") == 0;
     }();
     return use_simt ? launch_chunk_simt(p, stream) : launch_chunk_mfma(p, stream);
+}
+
+// KDA_INVERSE=neumann selects the fp16 Neumann-product inverse in the MFMA
+// kernel (an ablation of the pages' choice); read at every call.
+int inverse_from_env()
+{
+    const char *e = std::getenv("KDA_INVERSE");
+    return e && std::strcmp(e, "neumann") == 0 ? kInverseNeumann : kInverseSubst;
 }
 
 // The segmented form: map (end states, then transition matrices), combine,

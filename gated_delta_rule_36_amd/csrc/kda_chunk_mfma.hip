@@ -60,6 +60,7 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int C = kChunk;
 constexpr int D = kHeadDim;
@@ -430,6 +431,7 @@ struct SolveWave {
     int64_t beta_chunk_bytes;  // C * H * 2
     uint32_t beta_lane;        // lane * H * 2 (lane < 16), else 0
     uint32_t st_beta;
+    uint32_t bq;  // beta of tokens 4 g4 .. 4 g4 + 3 (the Neumann inverse)
 
     // The beta logits of chunk x (rows past the end read token 0).
     __device__ uint32_t load_beta(int x) const
@@ -516,6 +518,50 @@ struct SolveWave {
         const uint32_t at = slot_base(tb_st + s2 * kTileCC);
         lds_st(at + kOffThi, pack_bf16x2(static_cast<float>(hi0), static_cast<float>(hi1)));
         lds_st(at + kOffTlo, pack_bf16x2(static_cast<float>(lo0), static_cast<float>(lo1)));
+    }
+
+    // T of chunk x for the whole chunk in one wave (wave 14), as the product
+    // (I + L)(I + L^2)(I + L^4)(I + L^8) with L = -A: A is strictly lower, so
+    // L^16 = 0 and the product is the whole Neumann series -- the inverse the
+    // chunk-size page describes under "Efficient 16x16 Matrix Inversion",
+    // with fp16 MFMA operands and fp32 accumulation as there.  An MFMA result
+    // (lane (j, g4) holding X[4 g4 + r][j]) is the B operand of X and the A
+    // operand of X^T as it stands, so each power is also formed transposed
+    // and no value moves between lanes; the last product gives T^T, i.e. row
+    // l16 of T in lane (l16, g4), the layout T diag(beta) is stored in.
+    __device__ void solve_neumann(int x) const
+    {
+        const uint32_t s2 = x & 1, s3 = x % 3;
+        f32x4_t eye;  // the identity in either layout: (l16 == 4 g4 + r)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) eye[r] = (l16 == 4 * g4 + r) ? 1.0f : 0.0f;
+        const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+        auto h = [](f32x4_t v) { return __builtin_convertvector(v, f16x4_t); };
+        auto mm = [&](f16x4_t a, f16x4_t b) { return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, zero, 0, 0, 0); };
+        // L = -A as stored: row l16 (A operand), column l16 (B operand)
+        const f32x4_t la = lds_ld<f32x4_t>(slot_base(amat_ld + s2 * kTileA) + 16 * g4);
+        const uint32_t ac = slot_base(amat_st + s2 * kTileA);
+        f32x4_t lb;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) lb[r] = lds_ld<float>(ac + 4 * AP * r);
+        const f16x4_t LA = h(la), LB = h(lb);
+        const f32x4_t L2 = mm(LA, LB), L2T = mm(LB, LA);
+        const f16x4_t L2h = h(L2), L2Th = h(L2T);
+        const f32x4_t L4 = mm(L2Th, L2h), L4T = mm(L2h, L2Th);
+        const f32x4_t L8 = mm(h(L4T), h(L4));
+        const f32x4_t P = mm(h(L4T + eye), h(L8 + eye));  // (I + L^4)(I + L^8)
+        const f32x4_t Q = mm(h(L2T + eye), h(P));         // (I + L^2) P
+        const f32x4_t TT = mm(h(Q), h(la + eye));         // ((I + L) Q)^T
+        const f32x4_t tb = TT * lds_ld<f32x4_t>(bq + s3 * kTileBeta);  // T diag(beta), row l16
+        f32x4_t hi, lo;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            hi[r] = static_cast<float>(static_cast<__bf16>(tb[r]));
+            lo[r] = tb[r] - hi[r];
+        }
+        const uint32_t at = slot_base(r16 + s2 * kTileCC);
+        lds_st(at + kOffThi, pack_bf16x4(hi));
+        lds_st(at + kOffTlo, pack_bf16x4(lo));
     }
 
     // One multiply-add per step and column, with t_m read straight from lane
@@ -730,7 +776,7 @@ __device__ __forceinline__ void state_loop(StateWave &sw, int n_iter, int nc)
 // output pass, kChunkState for the segment end states, kChunkTransition for
 // the segment transition matrices).  One mode per kernel: with several state
 // loops in one kernel the compiler runs out of registers.
-template <int MODE>
+template <int MODE, int INV>
 __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
 {
     __shared__ Shared sh;
@@ -849,7 +895,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
                            reinterpret_cast<const char *>(p.beta + first),
                            C * p.H * 2,
                            lane < C ? static_cast<uint32_t>(lane * p.H * 2) : 0u,
-                           sh0 + kOffBeta + 4 * lane};
+                           sh0 + kOffBeta + 4 * lane,
+                           sh0 + kOffBeta + 16 * g4};
         __builtin_amdgcn_s_setprio(3);
         if (pw == 0) {
             // A of chunk it - 1 and WY of chunk it - 3 each iteration; the beta
@@ -886,8 +933,14 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
             if (pw == 1) {
                 if (it >= 1 && it - 1 < nc)
                     sv.p_stage(it - 1);
-            } else if (it >= 2 && it - 2 < nc)
-                sv.solve_stage(it - 2);
+            } else if (it >= 2 && it - 2 < nc) {
+                if constexpr (INV == kInverseNeumann) {
+                    if (pw == 2)
+                        sv.solve_neumann(it - 2);
+                } else {
+                    sv.solve_stage(it - 2);
+                }
+            }
             if (it >= 3 && it - 3 < nc)
                 sv.wy_stage(it - 3);
             lds_barrier();
@@ -953,9 +1006,15 @@ hipError_t launch_chunk_mfma(const FwdParams &p, hipStream_t stream)
 {
     const int64_t chains = p.num_seqs * p.H;
     const int64_t blocks = p.phase == kPhaseWhole ? chains : chains * p.n_seg;
-    const void *kernel = p.phase == kPhaseMapB   ? reinterpret_cast<const void *>(&chunk_mfma_kernel<kChunkState>)
-                         : p.phase == kPhaseMapM ? reinterpret_cast<const void *>(&chunk_mfma_kernel<kChunkTransition>)
-                                                 : reinterpret_cast<const void *>(&chunk_mfma_kernel<kChunkFull>);
+    const void *kernel;
+    if (p.inverse == kInverseNeumann)
+        kernel = p.phase == kPhaseMapB   ? reinterpret_cast<const void *>(&chunk_mfma_kernel<kChunkState, kInverseNeumann>)
+                 : p.phase == kPhaseMapM ? reinterpret_cast<const void *>(&chunk_mfma_kernel<kChunkTransition, kInverseNeumann>)
+                                         : reinterpret_cast<const void *>(&chunk_mfma_kernel<kChunkFull, kInverseNeumann>);
+    else
+        kernel = p.phase == kPhaseMapB   ? reinterpret_cast<const void *>(&chunk_mfma_kernel<kChunkState, kInverseSubst>)
+                 : p.phase == kPhaseMapM ? reinterpret_cast<const void *>(&chunk_mfma_kernel<kChunkTransition, kInverseSubst>)
+                                         : reinterpret_cast<const void *>(&chunk_mfma_kernel<kChunkFull, kInverseSubst>);
     FwdParams args = p;
     void *argv[] = {&args};
     return hipLaunchKernel(kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), argv, 0, stream);

@@ -12,6 +12,9 @@ constexpr int kHeadDim = 128;  // K = V = 128
 
 enum StateKind : int { kStateNone = 0, kStateBf16 = 1, kStateFp32 = 2 };
 enum Phase : int { kPhaseWhole = 0, kPhaseMapB = 1, kPhaseMapM = 2, kPhaseOut = 3 };
+// How the MFMA kernel forms T = (I + A)^-1: fp32 forward substitution (the
+// default) or the fp16 Neumann product (KDA_INVERSE=neumann; an ablation).
+enum Inverse : int { kInverseSubst = 0, kInverseNeumann = 1 };
 
 // Everything a launch needs.  Pointers are device pointers; sizes were
 // validated by the front end.
@@ -28,6 +31,7 @@ struct FwdParams {
     int64_t T, H;                          // token axis length, heads
     float scale;                           // read-out scale
     float gate_scale;                      // lower_bound * log2(e), in fp32
+    int inverse = kInverseSubst;           // Inverse (MFMA kernel)
 
     // Intra-sequence scan (kda_fwd_scan).  Every chain is cut into segments
     // of seg_chunks chunks; segment s maps its start state S to M_s S + b_s
@@ -47,6 +51,10 @@ struct FwdParams {
 
 // Enqueue the whole forward pass on `stream`.  Returns the launch status.
 hipError_t launch_forward(const FwdParams &p, hipStream_t stream);
+
+// The inverse method the environment selects (KDA_INVERSE=neumann), read at
+// every call.
+int inverse_from_env();
 
 // Enqueue the segmented form: map (phase 1), combine, output (phase 3).
 // p.seg_chunks, p.n_seg, p.seg_b and p.seg_m must be set.

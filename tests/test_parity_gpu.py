@@ -406,3 +406,64 @@ def test_scan_max_decay_and_no_decay():
                           device="cuda")
     print("[case] scan no decay", flush=True)
     check_full("scan no decay", y, torch.float32, segment_chunks=2)
+
+
+# --------------------------------------------------------------------------
+# the fp16 Neumann-product inverse (KDA_INVERSE=neumann): an ablation of the
+# pages' choice of inverse against the default fp32 forward substitution
+# --------------------------------------------------------------------------
+
+@pytest.fixture
+def neumann_inverse(monkeypatch):
+    monkeypatch.setenv("KDA_INVERSE", "neumann")
+
+
+def test_neumann_small_workload(neumann_inverse):
+    print("[case] neumann small workload", flush=True)
+    check_full("neumann small", synth.workload("small_b2_t128_h8", device="cuda"), torch.float32)
+
+
+@pytest.mark.parametrize("T", [1, 17, 100])
+def test_neumann_ragged(neumann_inverse, T):
+    print(f"[case] neumann T={T}", flush=True)
+    x = synth.make_inputs(2, T, 3, lower_bound=-5.0, seed=200 + T, init_dtype=torch.float32,
+                          device="cuda")
+    check_full(f"neumann T={T}", x, torch.float32)
+
+
+def test_neumann_varlen_and_scan(neumann_inverse):
+    lens = [1, 16, 17, 0, 33, 5, 48, 2, 130]
+    print("[case] neumann varlen + segmented form", flush=True)
+    x = synth.make_inputs(1, 0, 4, lower_bound=-5.0, seed=41, seq_lengths=lens,
+                          init_dtype=torch.bfloat16, device="cuda")
+    check_full("neumann varlen", x, torch.bfloat16)
+    check_full("neumann varlen scan", x, torch.bfloat16, segment_chunks=2)
+
+
+def test_neumann_gate_extremes(neumann_inverse):
+    """No decay with beta ~ 1 gives the largest entries of T; full decay the
+    smallest operands."""
+    x = synth.make_inputs(1, 64, 2, lower_bound=-5.0, seed=42, init_dtype=torch.float32,
+                          device="cuda")
+    x.g.fill_(-100.0)
+    x.beta.fill_(8.0)
+    print("[case] neumann min decay, large beta", flush=True)
+    check_full("neumann min decay", x, torch.float32)
+    y = synth.make_inputs(2, 96, 4, lower_bound=-5.0, seed=43, init_dtype=torch.float32,
+                          device="cuda")
+    y.g.fill_(100.0)
+    print("[case] neumann max decay", flush=True)
+    check_full("neumann max decay", y, torch.float32)
+
+
+def test_inverse_choice_is_read_per_call(monkeypatch):
+    """The two inverses give different roundings, and the selection follows
+    the environment at every call."""
+    x = synth.make_inputs(1, 64, 2, lower_bound=-5.0, seed=44, device="cuda")
+    o_sub, _ = run_gpu(x)
+    monkeypatch.setenv("KDA_INVERSE", "neumann")
+    o_neu, _ = run_gpu(x)
+    monkeypatch.delenv("KDA_INVERSE")
+    o_sub2, _ = run_gpu(x)
+    assert np.array_equal(o_sub, o_sub2)
+    assert not np.array_equal(o_sub, o_neu)
