@@ -22,11 +22,14 @@
 //                update.  S is the B operand of W S and Qt S through a fixed
 //                permutation of the contraction index, so the fp32
 //                accumulators convert to bf16 operands in place.
-//   waves 4-11   gate waves.  Loads: every gate wave moves a quarter-tensor
-//                slab (8 token rows of q, k, g or v) of each chunk straight
-//                into LDS with direct global-to-LDS loads two chunks ahead,
-//                whole 128-byte lines per request (q, k, g into a staging
-//                ring, v into its ring for the WY stage).  Compute: wave 4 + c
+//   waves 4-11   gate waves.  Loads: waves 4-7 each move half of q or k (8
+//                token rows) of each chunk straight into LDS with direct
+//                global-to-LDS loads two chunks ahead, whole 128-byte lines
+//                per request, into a staging ring (g and v are loaded the
+//                same way by wave 13, v into its ring for the WY stage; the
+//                loads sit on the waves that finish their stage early, so
+//                no wave at the end of an iteration waits for memory).
+//                Compute: wave 4 + c
 //                owns channels 16c..16c+15: it reads its q, k, g channel-major
 //                through transposing LDS reads, computes the gate, the
 //                cumulative decay products and the decayed operands, and
@@ -66,7 +69,6 @@ constexpr int C = kChunk;
 constexpr int D = kHeadDim;
 constexpr int kThreads = 1024;  // 4 state waves, 8 gate waves, 4 solve waves
 constexpr int kStages = 4;      // iterations between the gate and the state stage of a chunk
-constexpr int kLoadsPerChunk = 2;  // DMAs per gate wave and chunk
 
 // LDS bank layout.  gfx950 serves 64-bit reads 32 lanes at a time from 64
 // banks, 128-bit reads in four passes, and writes 16 lanes at a time into
@@ -168,6 +170,7 @@ constexpr uint32_t kTileU = D * C * 4;         // U~ tile (fp32)
 constexpr uint32_t kTileCC = C * C * 2;        // 16 x 16 bf16 (P, T parts)
 constexpr uint32_t kTileA = C * AP * 4;        // -A (fp32)
 constexpr uint32_t kTileGam = D * 4, kTileBeta = C * 4;
+static_assert(kTileGam * 8 == kTile, "the Gamma_C ring offset is the tile ring offset / 8");
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
 {
@@ -301,24 +304,62 @@ __device__ __forceinline__ void dma16(const char *base, uint32_t voff, uint32_t 
     asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(dst) : "memory");
 }
 
+// Direct loads of 4 NJ token rows of one tensor per chunk into an LDS ring,
+// 4 rows (1 KB) per load: lane i takes 16-byte chunk (i % 16) ^ r of row
+// r = row0 + 4 j + i / 16, which lands at position i % 16 of the row: the
+// swizzled token-major layout.  Rows past the sequence end take token 0's
+// data.  The cursor (chunk, source, ring slot) advances one chunk per
+// iteration up to the last chunk, so the loop needs no per-chunk multiplies
+// or remainders.  Bases and strides are wave-uniform (scalar registers).
+template <int NJ>
+struct Loader {
+    const char *src;              // the tensor at chunk x
+    int64_t chunk_bytes;          // between consecutive chunks: C * H * 256
+    uint32_t full[NJ], tail[NJ];  // lane offsets; rows past a partial last chunk on token 0
+    uint32_t dst, dst0, dst_end;  // LDS: chunk x's slot (row row0), the ring's first slot, its end
+    uint32_t slot;                // bytes between ring slots
+    int x, n_full;                // chunk being loaded; full chunks of the range
+
+    __device__ void init(const uint16_t *tensor, int64_t tok_bytes, int row0, int lane, int tail_len,
+                         int nfull, uint32_t ring0, uint32_t slot_bytes, int ring)
+    {
+        src = reinterpret_cast<const char *>(tensor);
+        chunk_bytes = C * tok_bytes;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int r = row0 + 4 * j + (lane >> 4), c = (lane & 15) ^ r;
+            full[j] = static_cast<uint32_t>(r * tok_bytes + 16 * c);
+            tail[j] = static_cast<uint32_t>((r < tail_len ? r : 0) * tok_bytes + 16 * c);
+        }
+        dst0 = ring0;
+        dst = ring0 + 256 * row0;
+        dst_end = ring0 + ring * slot_bytes;
+        slot = slot_bytes;
+        x = 0;
+        n_full = nfull;
+    }
+    // Start loading chunk x (NJ loads; every lane loads something valid).
+    __device__ void issue() const
+    {
+        const bool f = x < n_full;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) dma16(src, f ? full[j] : tail[j], dst + 1024 * j);
+    }
+    __device__ void advance(int nc)
+    {
+        if (x < nc - 1) {
+            ++x;
+            src += chunk_bytes;
+            dst = dst + slot >= dst_end ? dst - (dst_end - dst0) + slot : dst + slot;
+        }
+    }
+};
+
 struct GateWave {
     const FwdParams &p;
     int gc16;  // 0..7: channels 16 gc16 .. 16 gc16 + 15, wave-uniform
     int lane, l16, g4;
     int n_full, tail;  // full chunks of the sequence; length of a partial last chunk (0: none)
-    // Loads.  Gate wave gc16 moves rows 8 hf .. 8 hf + 7 (hf = gc16 & 1) of
-    // tensor gc16 / 2 (q, k, g, v) of every chunk into LDS, 4 rows (1 KB) per
-    // DMA: lane i takes 16-byte chunk (i % 16) ^ r of row r = 4 j + i / 16 of
-    // its pair, which lands at position i % 16 of the row: the swizzled
-    // token-major layout.  Rows past the sequence end take token 0's data.
-    // Bases and strides are wave-uniform (scalar registers).
-    const char *dma_src;       // the tensor at token t_begin
-    int64_t chunk_bytes;       // between consecutive chunks: C * H * 256
-    uint32_t dma_full[2];      // lane offsets of the two DMAs
-    uint32_t dma_tail[2];      // the same with rows past the end of a partial chunk on token 0
-    uint32_t dma_dst;          // LDS byte address of row 8 hf in slot 0 of the ring
-    uint32_t dma_slot;         // bytes between ring slots (stage or V ring)
-    int dma_ring;              // 3 (stage) or 6 (V ring)
     // LDS addresses (ring slot 0, without the ring's offset): this lane's
     // transposing read of channels 16 gc16 + 4 (l16 % 4) .. of token
     // 4 g4 + l16 / 4 in the stage tiles; its stores into the channel-major
@@ -331,38 +372,25 @@ struct GateWave {
 
     __device__ int chunk_len(int x) const { return x < n_full ? C : tail; }
 
-    // Start loading chunk x: two DMAs (kLoadsPerChunk) into its ring slot.
-    // Every lane loads something valid.
-    __device__ void issue(int x) const
-    {
-        uint32_t o0 = dma_full[0], o1 = dma_full[1];
-        if (x >= n_full) {
-            o0 = dma_tail[0];
-            o1 = dma_tail[1];
-        }
-        const char *src = dma_src + int64_t(x) * chunk_bytes;
-        const uint32_t dst = dma_dst + static_cast<uint32_t>(dma_ring == 6 ? x % 6 : x % 3) * dma_slot;
-        dma16(src, o0, dst);
-        dma16(src, o1, dst + 1024);
-    }
-
     // Gate, decay products and decayed operands of chunk x for this wave's
     // 16 channels.  FULL: all 16 rows of the chunk lie in the sequence.
-    __device__ void gate_stage(int x) const
+    // o3, o5: offsets of chunk x's stage slot and of its Qt / Kbar ring slot
+    // (x mod 3 and x mod 5 slots, kept as running offsets by the caller).
+    __device__ void gate_stage(int x, uint32_t o3, uint32_t o5) const
     {
         if (x < n_full)
-            gate_rows<true>(x);
+            gate_rows<true>(x, o3, o5);
         else
-            gate_rows<false>(x);
+            gate_rows<false>(x, o3, o5);
     }
     template <bool FULL>
-    __device__ void gate_rows(int x) const
+    __device__ void gate_rows(int x, uint32_t o3, uint32_t o5) const
     {
         const int len = FULL ? C : tail;
-        const uint32_t s2 = x & 1, s3 = x % 3, s4 = x & 3, s5 = x % 5;
+        const uint32_t s2 = x & 1, s4 = x & 3;
         // channel-major: the transposing read of the token-major stage tiles
         // gives lane (l16, g4) tokens 4 g4 .. 4 g4 + 3 of channel 16 gc16 + l16
-        const uint32_t ar = slot_base(rd_stage + s3 * (3 * kTile));
+        const uint32_t ar = slot_base(rd_stage + o3);
         const f32x4_t cq = bf16x4_to_f32(lds_tr(ar));
         const f32x4_t ck = bf16x4_to_f32(lds_tr(ar + kTile));
         const f32x4_t cg = bf16x4_to_f32(lds_tr(ar + 2 * kTile));
@@ -399,13 +427,13 @@ struct GateWave {
             kb[i] = ck[i] * gbar[i];
             kh[i] = kb[i] * inv_gc;
         }
-        const uint32_t a5 = slot_base(st_col + s5 * kTile);  // Qt and Kbar share the ring index
+        const uint32_t a5 = slot_base(st_col + o5);  // Qt and Kbar share the ring index
         lds_st(slot_base(st_col + s4 * kTile) + kOffKt, pack_bf16x4(kt));
         lds_st(slot_base(st_col + s2 * kTile) + kOffKh, pack_bf16x4(kh));
         lds_st(a5 + kOffQt, pack_bf16x4(qt));
         lds_st(a5 + kOffKb, pack_bf16x4(kb));
         if (g4 == 0)
-            lds_st(st_gam + s5 * kTileGam, gc);
+            lds_st(st_gam + (o5 >> 3), gc);
     }
 };
 
@@ -927,13 +955,43 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
             wait_vmem<0>();  // no load may still be writing registers when the wave ends
             return;
         }
-        if (n_iter > 0)
-            lds_barrier();  // the gate waves' first loads are in LDS
-        for (int it = 0; it < n_iter; ++it) {
-            if (pw == 1) {
+        if (pw == 1) {
+            // P of chunk it - 1 and WY of chunk it - 3 each iteration; this
+            // wave also loads all 16 rows of g and v two chunks ahead (g into
+            // the stage ring, v into its ring for WY), like the gate waves'
+            // loads of q and k.
+            Loader<4> lg, lv;
+            lg.init(p.g + first * D, tok_bytes, 0, lane, tail, n_full, sh0 + kOffStage + 2 * kTile, 3 * kTile, 3);
+            lv.init(p.v + first * D, tok_bytes, 0, lane, tail, n_full, sh0 + kOffV, kTile, 6);
+            if (n_iter > 0) {
+                for (int c = 0; c < 2; ++c) {  // chunks 0 and min(1, nc - 1)
+                    lg.issue();
+                    lv.issue();
+                    lg.advance(nc);
+                    lv.advance(nc);
+                }
+                wait_vmem<8>();  // chunk 0
+                lds_barrier();
+            }
+            for (int it = 0; it < n_iter; ++it) {
+                lg.issue();  // chunk min(it + 2, nc - 1); slots as for the gate waves' loads
+                lv.issue();
+                lg.advance(nc);
+                lv.advance(nc);
                 if (it >= 1 && it - 1 < nc)
                     sv.p_stage(it - 1);
-            } else if (it >= 2 && it - 2 < nc) {
+                if (it >= 3 && it - 3 < nc)
+                    sv.wy_stage(it - 3);
+                wait_vmem<8>();  // chunk it + 1
+                lds_barrier();
+            }
+            wait_vmem<0>();  // no load may still be writing LDS when the wave ends
+            return;
+        }
+        if (n_iter > 0)
+            lds_barrier();  // the first loads are in LDS
+        for (int it = 0; it < n_iter; ++it) {
+            if (it >= 2 && it - 2 < nc) {
                 if constexpr (INV == kInverseNeumann) {
                     if (pw == 2)
                         sv.solve_neumann(it - 2);
@@ -949,22 +1007,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
     }
 
     // gate waves
-    const int gc16 = wave - 4, tens = gc16 >> 1, hf = gc16 & 1;
-    const uint16_t *const tensor = tens == 0 ? p.q : tens == 1 ? p.k : tens == 2 ? p.g : p.v;
-    uint32_t dma_full[2], dma_tail[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int r = 8 * hf + 4 * j + (lane >> 4), c = (lane & 15) ^ r;
-        dma_full[j] = static_cast<uint32_t>(r * tok_bytes + 16 * c);
-        dma_tail[j] = static_cast<uint32_t>((r < tail ? r : 0) * tok_bytes + 16 * c);
-    }
+    const int gc16 = wave - 4;
     GateWave gw{p, gc16, lane, l16, g4, n_full, tail,
-                reinterpret_cast<const char *>(tensor + first * D),
-                C * tok_bytes,
-                {dma_full[0], dma_full[1]}, {dma_tail[0], dma_tail[1]},
-                sh0 + (tens < 3 ? kOffStage + tens * kTile : kOffV) + 2 * D * 8 * hf,
-                tens < 3 ? 3 * kTile : kTile,
-                tens < 3 ? 3 : 6,
                 sh0 + kOffStage + chan_lane(16 * gc16, l16, g4),
                 sh0 + 512 * gc16 + row16_lane(l16, g4),
                 sh0 + kOffGam + 4 * (16 * gc16 + l16)};
@@ -979,21 +1023,37 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
     // The stage ring holds three chunks: iteration `it` starts the loads of
     // chunk it + 2, runs the gate stage on chunk it and, before the barrier,
     // waits for the loads of chunk it + 1 (issued one iteration earlier), so
-    // every chunk has two iterations to arrive.  Past the last chunk the stage runs
-    // on a repeat of it and fills only ring slots that no later stage reads.
-    // The state and solve waves (priority 3) sit on the critical path; the
-    // gate waves fill the issue slots they leave.
+    // every chunk has two iterations to arrive.  Past the last chunk the stage
+    // runs on a repeat of it and fills only ring slots that no later stage
+    // reads.  Waves 4-7 load rows 8 (gc16 % 2) .. + 7 of q (waves 4, 5) or k
+    // (6, 7); waves 8-11 load nothing.  The state and solve waves (priority
+    // 3) sit on the critical path; the gate waves fill the issue slots they
+    // leave.
     __builtin_amdgcn_s_setprio(1);
-    gw.issue(0);
-    gw.issue(nc > 1 ? 1 : 0);
-    wait_vmem<kLoadsPerChunk>();
+    const bool loads = gc16 < 4;
+    Loader<2> ld;
+    ld.init((gc16 < 2 ? p.q : p.k) + first * D, tok_bytes, 8 * (gc16 & 1), lane, tail, n_full,
+            sh0 + kOffStage + (gc16 >> 1) * kTile, 3 * kTile, 3);
+    if (loads) {
+        for (int c = 0; c < 2; ++c) {  // chunks 0 and min(1, nc - 1)
+            ld.issue();
+            ld.advance(nc);
+        }
+    }
+    wait_vmem<2>();  // chunk 0 (a no-op for the waves that load nothing)
     lds_barrier();
+    uint32_t o3 = 0, o5 = 0;  // chunk it's stage slot and Qt / Kbar slot
     for (int it = 0; it < n_iter; ++it) {
         // slot of chunk it + 2 (stage: last read by the gate stage of chunk
         // it - 1; V: by WY of chunk it - 4, both before the last barrier)
-        gw.issue(it + 2 < nc ? it + 2 : nc - 1);
-        gw.gate_stage(it);
-        wait_vmem<kLoadsPerChunk>();
+        if (loads) {
+            ld.issue();
+            ld.advance(nc);
+        }
+        gw.gate_stage(it, o3, o5);
+        o3 = o3 == 2 * (3 * kTile) ? 0 : o3 + 3 * kTile;
+        o5 = o5 == 4 * kTile ? 0 : o5 + kTile;
+        wait_vmem<2>();  // chunk it + 1
         lds_barrier();
     }
     // no load may still be writing LDS when the wave ends
