@@ -3,7 +3,9 @@
 One step = one forward call over the whole workload (every stage of the
 forward pass runs inside it), inputs already resident in HBM: ``kda_fwd``,
 or for workloads with few chains the segmented form ``kda_fwd_scan``
-(``--segment-chunks``; its four launches together make the step).  The default
+(``--segment-chunks``; its four launches together make the step).
+``kda_fwd`` runs the chunked kernel, or for decode-shaped workloads (at most
+16 tokens per sequence) the recurrent one; ``config.kernel`` names it.  The default
 workload is the large throughput case: B=8, T=16384, H=32, K=V=128,
 lower_bound=-5, scale=1/sqrt(128), fp32 final_state written, no initial
 state.  Prints one JSON line:
@@ -29,7 +31,7 @@ import time
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic_large_b8_t16384_h32.json")
+PROFILES = os.path.join(HERE, "profiles")
 
 
 def source_digest() -> str:
@@ -60,15 +62,16 @@ def algorithmic_bytes(x, final_dtype) -> int:
     return n
 
 
-def stored_traffic(launch_bytes: int):
-    """HBM bytes per launch from committed rocprofv3 counters, if they were
-    taken on the current kernel sources; else None."""
+def stored_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of this workload from committed rocprofv3
+    counters (profiles/traffic_<workload>.json), if they were taken on the
+    current kernel sources and the same kernel; else None."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(os.path.join(PROFILES, f"traffic_{workload}.json")) as fh:
             rec = json.load(fh)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != source_digest():
+    if rec.get("source_sha256") != source_digest() or rec.get("kernel_choice") != kernel:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -178,7 +181,8 @@ def main():
     avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
     launch_bytes = algorithmic_bytes(x, final_dtype)
     achieved = launch_bytes / avg_launch_s / 1e9
-    traffic = stored_traffic(launch_bytes)
+    kernel = "mfma (segmented)" if seg else kda.fwd_kernel(T, x.cu_seqlens is not None)
+    traffic = stored_traffic(args.workload, kernel)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel_ms": round(avg_launch_s * 1e3, 4), "bytes_per_launch": launch_bytes}
@@ -200,7 +204,8 @@ def main():
                    "lower_bound": x.lower_bound, "varlen": x.cu_seqlens is not None,
                    "initial_state": None if x.initial_state is None else str(x.initial_state.dtype),
                    "final_state": None if final_dtype is None else str(final_dtype),
-                   "segment_chunks": seg},
+                   "segment_chunks": seg,
+                   "kernel": kernel},
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:

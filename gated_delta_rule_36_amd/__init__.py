@@ -6,6 +6,6 @@ run every step of the forward pass.  ``synth`` draws the seeded synthetic
 inputs of the named workloads.
 """
 from ._lib import KdaLibraryMissing
-from .api import KdaArgumentError, KdaError, auto_segment_chunks, fwd
+from .api import KdaArgumentError, KdaError, auto_segment_chunks, fwd, fwd_kernel
 
-__all__ = ["fwd", "auto_segment_chunks", "KdaError", "KdaArgumentError", "KdaLibraryMissing"]
+__all__ = ["fwd", "fwd_kernel", "auto_segment_chunks", "KdaError", "KdaArgumentError", "KdaLibraryMissing"]

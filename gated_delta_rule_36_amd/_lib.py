@@ -8,8 +8,8 @@ LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
 # Every symbol include/kda.h declares.
 EXPORTS = ("kda_fwd", "kda_fwd_scan", "kda_fwd_scan_workspace_bytes", "kda_status_string",
-           "kda_abi_version")
-ABI_VERSION = 2
+           "kda_fwd_kernel", "kda_abi_version")
+ABI_VERSION = 3
 
 # kda_status codes (include/kda.h)
 KDA_OK = 0
@@ -57,6 +57,8 @@ def load() -> ctypes.CDLL:
     lib.kda_fwd_scan_workspace_bytes.restype = i64
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_fwd_kernel.argtypes = [i64, ctypes.c_int]
+    lib.kda_fwd_kernel.restype = ctypes.c_char_p
     lib.kda_abi_version.argtypes = []
     lib.kda_abi_version.restype = ctypes.c_int
     if lib.kda_abi_version() != ABI_VERSION:

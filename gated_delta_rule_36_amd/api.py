@@ -166,6 +166,14 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
     return out
 
 
+def fwd_kernel(T: int, varlen: bool = False) -> str:
+    """Name of the kernel ``fwd`` runs for a call with ``T`` tokens per batch
+    row (``varlen``: cu_seqlens given), as the library decides it (including
+    the KDA_KERNEL override): "recurrent", "mfma" or "simt".  The segmented
+    form (``segment_chunks``) always runs the chunked kernel."""
+    return _lib.load().kda_fwd_kernel(int(T), 1 if varlen else 0).decode()
+
+
 def auto_segment_chunks(chains: int, T: int, target_blocks: int = 256,
                         min_chunks: int = 8, min_segments: int = 6) -> Optional[int]:
     """Segment length (in 16-token chunks) for the segmented form, or None

@@ -238,15 +238,32 @@ extern "C" const char *kda_status_string(kda_status status)
 extern "C" int kda_abi_version(void) { return KDA_ABI_VERSION; }
 
 namespace kda {
-// The MFMA kernel is the forward pass.  KDA_KERNEL=simt selects the plain
-// fp32 kernel instead (same results within rounding; for cross-checks).
+// Kernel choice, read at every call.  By default calls without cu_seqlens
+// and with at most kDecodeMaxTokens tokens per sequence (decode-shaped: the
+// state traffic dominates) take the recurrent kernel, everything else the
+// chunked MFMA kernel.  KDA_KERNEL=mfma, =recurrent or =simt (the plain fp32
+// chunked kernel, for cross-checks) forces one for every call.
+enum KernelChoice { kKernelMfma, kKernelRecurrent, kKernelSimt };
+
+static KernelChoice kernel_choice(int64_t T, bool varlen)
+{
+    const char *e = std::getenv("KDA_KERNEL");
+    if (e && std::strcmp(e, "simt") == 0)
+        return kKernelSimt;
+    if (e && std::strcmp(e, "recurrent") == 0)
+        return kKernelRecurrent;
+    if (e && std::strcmp(e, "mfma") == 0)
+        return kKernelMfma;
+    return !varlen && T <= kDecodeMaxTokens ? kKernelRecurrent : kKernelMfma;
+}
+
 hipError_t launch_forward(const FwdParams &p, hipStream_t stream)
 {
-    static const bool use_simt = [] {
-        const char *e = std::getenv("KDA_KERNEL");
-        return e && std::strcmp(e, "simt") == 0;
-    }();
-    return use_simt ? launch_chunk_simt(p, stream) : launch_chunk_mfma(p, stream);
+    switch (kernel_choice(p.T, p.cu_seqlens != nullptr)) {
+    case kKernelSimt: return launch_chunk_simt(p, stream);
+    case kKernelRecurrent: return launch_decode(p, stream);
+    default: return launch_chunk_mfma(p, stream);
+    }
 }
 
 // KDA_INVERSE=neumann selects the fp16 Neumann-product inverse in the MFMA
@@ -277,3 +294,12 @@ hipError_t launch_forward_scan(const FwdParams &p, hipStream_t stream)
     return err;
 }
 }  // namespace kda
+
+extern "C" const char *kda_fwd_kernel(int64_t T, int varlen)
+{
+    switch (kda::kernel_choice(T, varlen != 0)) {
+    case kda::kKernelSimt: return "simt";
+    case kda::kKernelRecurrent: return "recurrent";
+    default: return "mfma";
+    }
+}

@@ -170,8 +170,20 @@ int64_t kda_fwd_scan_workspace_bytes(const int64_t *cu_seqlens, int64_t num_seqs
 /* Static, NUL-terminated description of a status code. */
 const char *kda_status_string(kda_status status);
 
+/*
+ * Name of the kernel kda_fwd runs for a call with T tokens per batch row
+ * (varlen != 0: cu_seqlens given).  "recurrent": the token recurrence itself,
+ * one small workgroup per chain, for decode-shaped calls (no cu_seqlens and
+ * T <= 16), where the state traffic dominates; "mfma": the chunked kernel,
+ * for everything else.  The environment variable KDA_KERNEL (mfma,
+ * recurrent, or simt: a plain fp32 chunked kernel kept for cross-checks),
+ * read at every call, overrides the choice.  Returns a static string; pure
+ * host logic, no device work.  kda_fwd_scan always runs the chunked kernel.
+ */
+const char *kda_fwd_kernel(int64_t T, int varlen);
+
 /* ABI version of this header (bumped on any signature change). */
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 int kda_abi_version(void);
 
 #ifdef __cplusplus

@@ -178,6 +178,22 @@ def test_auto_segment_chunks_policy():
     assert auto(0, 1000) is None
 
 
+def test_kernel_choice(monkeypatch):
+    """Decode-shaped calls (no cu_seqlens, at most 16 tokens) take the
+    recurrent kernel, everything else the chunked one; KDA_KERNEL overrides
+    the choice and is read at every call."""
+    monkeypatch.delenv("KDA_KERNEL", raising=False)
+    choice = kda.fwd_kernel
+    assert [choice(t) for t in (0, 1, 8, 15, 16)] == ["recurrent"] * 5
+    assert [choice(t) for t in (17, 64, 16384)] == ["mfma"] * 3
+    assert choice(1, varlen=True) == choice(16, varlen=True) == "mfma"
+    for forced in ("mfma", "recurrent", "simt"):
+        monkeypatch.setenv("KDA_KERNEL", forced)
+        assert choice(1) == choice(10000) == choice(5, varlen=True) == forced
+    monkeypatch.setenv("KDA_KERNEL", "no-such-kernel")
+    assert choice(1) == "recurrent" and choice(17) == "mfma"
+
+
 def test_empty_token_tensors_may_be_null():
     """With T = 0 the token tensors are empty (torch gives them a NULL data
     pointer), which is accepted; packed mode with no sequence launches

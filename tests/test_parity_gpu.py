@@ -146,9 +146,14 @@ def test_large_workload_parity_sampled_chains():
 # edges: ragged tails, empty inputs, extreme gates, state dtypes
 # --------------------------------------------------------------------------
 
+@pytest.mark.parametrize("kernel", [None, "mfma"])
 @pytest.mark.parametrize("T", [0, 1, 15, 16, 17, 33, 100])
-def test_chunk_edges(T):
-    print(f"[case] chunk edge T={T}", flush=True)
+def test_chunk_edges(T, kernel, monkeypatch):
+    """Short calls take the recurrent kernel by default; KDA_KERNEL=mfma
+    keeps the chunked kernel covered on the same shapes."""
+    if kernel:
+        monkeypatch.setenv("KDA_KERNEL", kernel)
+    print(f"[case] chunk edge T={T} kernel={kernel or 'default'}", flush=True)
     x = synth.make_inputs(2, T, 3, lower_bound=-5.0, seed=T, init_dtype=torch.float32,
                           device="cuda")
     o, f = run_gpu(x, torch.float32)
@@ -263,7 +268,12 @@ def test_split_sequence_chaining(split):
         assert_close("split final", f2, f)
 
 
-def test_packed_equals_separate_runs():
+@pytest.mark.parametrize("kernel", ["mfma", "recurrent"])
+def test_packed_equals_separate_runs(kernel, monkeypatch):
+    """Packed sequences give exactly the results of separate calls on the
+    same kernel (short separate calls would otherwise take the recurrent
+    kernel, so the kernel is pinned)."""
+    monkeypatch.setenv("KDA_KERNEL", kernel)
     lens = [20, 3, 35, 16]
     x = synth.make_inputs(1, 0, 2, lower_bound=-5.0, seed=19, seq_lengths=lens,
                           init_dtype=torch.float32, device="cuda")
@@ -416,6 +426,7 @@ def test_scan_max_decay_and_no_decay():
 @pytest.fixture
 def neumann_inverse(monkeypatch):
     monkeypatch.setenv("KDA_INVERSE", "neumann")
+    monkeypatch.setenv("KDA_KERNEL", "mfma")  # short calls would take the recurrent kernel
 
 
 def test_neumann_small_workload(neumann_inverse):
@@ -467,3 +478,133 @@ def test_inverse_choice_is_read_per_call(monkeypatch):
     o_sub2, _ = run_gpu(x)
     assert np.array_equal(o_sub, o_sub2)
     assert not np.array_equal(o_sub, o_neu)
+
+
+# --------------------------------------------------------------------------
+# the recurrent kernel (decode-shaped calls; KDA_KERNEL=recurrent forces it
+# for any call, which covers several 8-token passes, tails and packed input)
+# --------------------------------------------------------------------------
+
+@pytest.fixture
+def recurrent_kernel(monkeypatch):
+    monkeypatch.setenv("KDA_KERNEL", "recurrent")
+
+
+@pytest.mark.parametrize("name", ["decode_b64_t1_h32_state", "decode_b64_t8_h32_state",
+                                  "decode_b64_t15_h32_state"])
+def test_decode_workloads_on_the_chunked_kernel(name, monkeypatch):
+    """The decode workloads take the recurrent kernel by default; the chunked
+    kernel must agree with the oracle on them too."""
+    monkeypatch.setenv("KDA_KERNEL", "mfma")
+    print(f"[case] workload {name} on the chunked kernel", flush=True)
+    x = synth.workload(name, device="cuda")
+    check_full(f"{name} mfma", x, x.final_dtype)
+
+
+@pytest.mark.parametrize("T", [0, 1, 7, 8, 9, 16, 17, 33, 100])
+def test_recurrent_lengths(recurrent_kernel, T):
+    print(f"[case] recurrent T={T}", flush=True)
+    x = synth.make_inputs(2, T, 3, lower_bound=-5.0, seed=300 + T, init_dtype=torch.float32,
+                          device="cuda")
+    o, f = run_gpu(x, torch.float32)
+    ro, rf = oracle_of(x)
+    if T:
+        assert_close(f"recurrent T={T} out", o, ro)
+    assert_close(f"recurrent T={T} final", f, rf)
+
+
+@pytest.mark.parametrize("state", [torch.bfloat16, torch.float32])
+def test_recurrent_varlen(recurrent_kernel, state):
+    lens = [1, 16, 17, 0, 33, 5, 48, 2, 8, 9]
+    print(f"[case] recurrent varlen {lens} state={state}", flush=True)
+    x = synth.make_inputs(1, 0, 4, lower_bound=-5.0, seed=51, seq_lengths=lens,
+                          init_dtype=state, device="cuda")
+    check_full(f"recurrent varlen {state}", x, state)
+
+
+@pytest.mark.parametrize("lb", [0.0, -5.0, -0.5])
+def test_recurrent_lower_bound_values(recurrent_kernel, lb):
+    print(f"[case] recurrent lower_bound={lb}", flush=True)
+    x = synth.make_inputs(2, 15, 4, lower_bound=lb, seed=52, init_dtype=torch.float32,
+                          device="cuda")
+    check_full(f"recurrent lb={lb}", x, torch.float32)
+
+
+def test_recurrent_gate_extremes(recurrent_kernel):
+    """Full decay on every channel and token (the widest range of the
+    factored state within a pass), then no decay with beta ~ 1."""
+    x = synth.make_inputs(2, 40, 4, lower_bound=-5.0, seed=53, init_dtype=torch.float32,
+                          device="cuda")
+    x.g.fill_(100.0)
+    print("[case] recurrent max decay", flush=True)
+    check_full("recurrent max decay", x, torch.float32)
+    y = synth.make_inputs(1, 40, 2, lower_bound=-5.0, seed=54, init_dtype=torch.float32,
+                          device="cuda")
+    y.g.fill_(-100.0)
+    y.beta.fill_(8.0)
+    print("[case] recurrent min decay, large beta", flush=True)
+    check_full("recurrent min decay", y, torch.float32)
+
+
+def test_recurrent_without_gate_params(recurrent_kernel):
+    print("[case] recurrent A_log/dt_bias None", flush=True)
+    x = synth.make_inputs(2, 12, 2, lower_bound=-4.0, seed=55, with_gate_params=False,
+                          device="cuda")
+    check_full("recurrent no gate params", x, torch.bfloat16)
+
+
+@pytest.mark.parametrize("init,final", [(None, torch.bfloat16), (torch.bfloat16, torch.bfloat16),
+                                        (torch.float32, None), (None, None),
+                                        (torch.float32, torch.float32)])
+def test_recurrent_state_combinations(recurrent_kernel, init, final):
+    print(f"[case] recurrent init={init} final={final}", flush=True)
+    x = synth.make_inputs(1, 11, 3, lower_bound=-5.0, seed=56, init_dtype=init, device="cuda")
+    o, f = run_gpu(x, final)
+    ro, rf = oracle_of(x)
+    assert_close("recurrent state combo out", o, ro)
+    if final is not None:
+        assert_close("recurrent state combo final", f, rf)
+
+
+def test_recurrent_in_place_state(recurrent_kernel):
+    x = synth.make_inputs(3, 5, 3, lower_bound=-5.0, seed=57, init_dtype=torch.float32,
+                          device="cuda")
+    o, f = run_gpu(x, torch.float32)
+    st = x.initial_state.clone()
+    out = torch.empty_like(x.v)
+    kda.fwd(x.q, x.k, x.v, x.g, x.beta, x.scale, out, x.A_log, x.dt_bias, x.lower_bound,
+            initial_state=st, final_state=st)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.double().cpu().numpy(), o)
+    assert np.array_equal(st.double().cpu().numpy(), f)
+
+
+def test_recurrent_invariants(recurrent_kernel):
+    """Deterministic, and exactly linear in (v, initial_state) under scaling
+    by 2 (every rounding step commutes with it)."""
+    x = synth.make_inputs(2, 13, 4, lower_bound=-5.0, seed=58, init_dtype=torch.float32,
+                          device="cuda")
+    o1, f1 = run_gpu(x, torch.float32)
+    o2, f2 = run_gpu(x, torch.float32, out_fill=1.0)
+    assert np.array_equal(o1, o2) and np.array_equal(f1, f2)
+    x2 = synth.KdaInputs(**{**x.__dict__, "v": x.v * 2, "initial_state": x.initial_state * 2})
+    o3, f3 = run_gpu(x2, torch.float32)
+    assert np.array_equal(o3, 2 * o1) and np.array_equal(f3, 2 * f1)
+
+
+def test_kernel_choice_is_read_per_call(monkeypatch):
+    """A 5-token call takes the recurrent kernel unless KDA_KERNEL says
+    otherwise; the two kernels round differently and agree within the
+    tolerance."""
+    x = synth.make_inputs(2, 5, 3, lower_bound=-5.0, seed=59, init_dtype=torch.float32,
+                          device="cuda")
+    o_def, f_def = run_gpu(x, torch.float32)
+    monkeypatch.setenv("KDA_KERNEL", "recurrent")
+    o_rec, f_rec = run_gpu(x, torch.float32)
+    monkeypatch.setenv("KDA_KERNEL", "mfma")
+    o_mf, f_mf = run_gpu(x, torch.float32)
+    monkeypatch.delenv("KDA_KERNEL")
+    assert np.array_equal(o_def, o_rec) and np.array_equal(f_def, f_rec)
+    assert not np.array_equal(f_rec, f_mf)
+    assert_close("recurrent vs chunked out", o_rec, o_mf)
+    assert_close("recurrent vs chunked final", f_rec, f_mf)
