@@ -23,6 +23,7 @@ KDA_ERR_SIZE = 7
 KDA_ERR_SCALE = 8
 KDA_ERR_LAUNCH = 9
 KDA_ERR_WORKSPACE = 10
+KDA_ERR_ALIGNMENT = 11
 
 # kda_dtype codes
 KDA_DTYPE_NONE = 0

@@ -99,6 +99,16 @@ kda_status check_args(const void *q, const void *k, const void *v, const void *g
         return KDA_ERR_ALIAS;
     if (sf.overlaps(si) && final_state != initial_state)
         return KDA_ERR_ALIAS;
+    // The kernels move q, k, v, g, out and the states in pieces of up to 16
+    // bytes; beta, A_log, dt_bias and cu_seqlens are read element by element.
+    const auto misaligned = [](const void *ptr, uintptr_t a) {
+        return ptr != nullptr && reinterpret_cast<uintptr_t>(ptr) % a != 0;
+    };
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(g, 16) ||
+        misaligned(out, 16) || misaligned(initial_state, 16) || misaligned(final_state, 16) ||
+        misaligned(beta, 2) || misaligned(A_log, 4) || misaligned(dt_bias, 4) ||
+        misaligned(cu_seqlens, 8))
+        return KDA_ERR_ALIGNMENT;
     for (const Span &s : inputs) c->spans[c->n_spans++] = s;
     c->spans[c->n_spans++] = so;
     c->spans[c->n_spans++] = sf;
@@ -231,6 +241,7 @@ extern "C" const char *kda_status_string(kda_status status)
     case KDA_ERR_SCALE: return "scale must be finite";
     case KDA_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
     case KDA_ERR_WORKSPACE: return "workspace is NULL, not 16-byte aligned, too small, or overlaps a tensor";
+    case KDA_ERR_ALIGNMENT: return "a tensor pointer is misaligned (q, k, v, g, out, states: 16 bytes; beta 2; A_log, dt_bias 4; cu_seqlens 8)";
     }
     return "unknown status";
 }

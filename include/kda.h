@@ -61,10 +61,15 @@ typedef enum kda_status {
                                   than 2^31-1 (sequence, head) chains */
     KDA_ERR_SCALE = 8,         /* scale is not finite */
     KDA_ERR_LAUNCH = 9,        /* the HIP runtime rejected the launch */
-    KDA_ERR_WORKSPACE = 10     /* kda_fwd_scan: workspace NULL, not 16-byte
+    KDA_ERR_WORKSPACE = 10,    /* kda_fwd_scan: workspace NULL, not 16-byte
                                   aligned, smaller than
                                   kda_fwd_scan_workspace_bytes(), or
                                   overlapping a tensor argument */
+    KDA_ERR_ALIGNMENT = 11     /* a non-NULL pointer is misaligned: q, k, v,
+                                  g, out, initial_state and final_state need
+                                  16 bytes, beta 2, A_log and dt_bias 4,
+                                  cu_seqlens 8 (allocator memory and whole
+                                  token rows of it always are) */
 } kda_status;
 
 /* Element type of initial_state / final_state. */

@@ -53,8 +53,8 @@ def test_library_has_gfx950_code_and_no_oracle():
 # C-ABI argument errors (host checks only; pointers are dummies)
 # --------------------------------------------------------------------------
 
-FAKE = [ctypes.create_string_buffer(64) for _ in range(12)]
-ADDR = [ctypes.addressof(b) for b in FAKE]
+FAKE = [ctypes.create_string_buffer(64 + 16) for _ in range(12)]
+ADDR = [(ctypes.addressof(b) + 15) & ~15 for b in FAKE]  # 16-byte aligned, like allocator memory
 
 
 def call(**over):
@@ -99,14 +99,22 @@ def call(**over):
     (dict(B=1 << 40, T=1 << 30), _lib.KDA_ERR_SIZE),
     (dict(scale=math.inf), _lib.KDA_ERR_SCALE),
     (dict(scale=math.nan), _lib.KDA_ERR_SCALE),
+    (dict(q=ADDR[0] + 8), _lib.KDA_ERR_ALIGNMENT),
+    (dict(g=ADDR[3] + 2), _lib.KDA_ERR_ALIGNMENT),
+    (dict(out=ADDR[5] + 4), _lib.KDA_ERR_ALIGNMENT),
+    (dict(beta=ADDR[4] + 1), _lib.KDA_ERR_ALIGNMENT),
+    (dict(dt_bias=ADDR[7] + 2), _lib.KDA_ERR_ALIGNMENT),
+    (dict(init=ADDR[8] + 8, init_dtype=1), _lib.KDA_ERR_ALIGNMENT),
+    (dict(final=ADDR[10] + 8, final_dtype=2), _lib.KDA_ERR_ALIGNMENT),
+    (dict(cu=ADDR[9] + 4, num_seqs=0), _lib.KDA_ERR_ALIGNMENT),
 ])
 def test_argument_errors_are_reported_before_launch(over, code):
     assert call(**over) == code
 
 
 def test_status_strings_are_distinct():
-    msgs = [_lib.status_string(c) for c in range(11)]
-    assert len(set(msgs)) == 11 and msgs[0] == "ok"
+    msgs = [_lib.status_string(c) for c in range(12)]
+    assert len(set(msgs)) == 12 and msgs[0] == "ok"
     assert _lib.status_string(123) == "unknown status"
 
 
@@ -133,8 +141,8 @@ def test_scan_workspace_bytes():
 
 # separate 4 KiB dummies: with T = 1 the declared spans (256 bytes per token
 # tensor) stay inside them, so only the planted overlap is seen
-BIG = [ctypes.create_string_buffer(1 << 12) for _ in range(12)]
-BADDR = [ctypes.addressof(b) for b in BIG]
+BIG = [ctypes.create_string_buffer((1 << 12) + 16) for _ in range(12)]
+BADDR = [(ctypes.addressof(b) + 15) & ~15 for b in BIG]
 
 
 def call_scan(seg=4, ws=None, ws_bytes=1 << 30, **over):
