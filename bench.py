@@ -15,10 +15,19 @@ state.  Prints one JSON line:
             once, outputs written once) / average launch time (HIP events on
             the launch stream), against 8 TB/s
   cpu_baseline  the fp64 CPU oracle timed on this host on a bounded sample of
-            the same workload (whole sequences of two batch rows)
+            the same workload (whole sequences of two batch rows), and on one
+            thread over two chains
+  copy_gbs  a plain 1 GiB device-to-device copy on the same GPU, for context
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--segment-chunks auto|off|N]
+                       [--segment-chunks auto|off|N] [--flush-cache]
+
+--flush-cache reads a 512 MiB buffer before every launch (outside its HIP
+events), so that no launch finds its inputs in L2 or the 256 MiB MALL (a read
+leaves clean lines, so the launch pays no write-back for the flush); the
+step time is then the mean of the per-launch event times instead of the wall
+clock over the timed steps.  Small workloads (the decode ones) are measured
+this way too.
 """
 from __future__ import annotations
 
@@ -31,6 +40,11 @@ import time
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
+# Algorithmic flops per head-token of the chunked method (multiply-add = 2):
+# per 16-token chunk and head 6 C K V (W S, Qt S, Kbar^T U) + 2 C^2 (3K + 2V)
+# (A, P, W, U~, P U) + K V (decay) + C^3 (inverse) = 1,921,024.
+FLOPS_PER_HEAD_TOKEN = 1921024 / 16
 PROFILES = os.path.join(HERE, "profiles")
 
 
@@ -91,15 +105,23 @@ def cpu_baseline(x, rows: int = 2):
     cu = cpu(x.cu_seqlens)
     N = rows if cu is None else cu.numel() - 1
     chains = [(n, h) for n in range(N) for h in range(H)]
+    args = (q, k, v, g, beta, x.scale, cpu(x.A_log), cpu(x.dt_bias), x.lower_bound)
     t0 = time.perf_counter()
-    kda_oracle(q, k, v, g, beta, x.scale, cpu(x.A_log), cpu(x.dt_bias), x.lower_bound,
-               initial_state=init, cu_seqlens=cu, chains=chains, threads=cores)
+    kda_oracle(*args, initial_state=init, cu_seqlens=cu, chains=chains, threads=cores)
     dt = time.perf_counter() - t0
     head_tokens = rows * T * H
+    # one thread, two chains of the first sequence
+    t0 = time.perf_counter()
+    kda_oracle(*args, initial_state=init, cu_seqlens=cu, chains=chains[:2], threads=1)
+    dt1 = time.perf_counter() - t0
+    seq_len = T if cu is None else int(cu[1] - cu[0])
     return {"value": head_tokens / dt, "unit": "head-tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{len(chains)} whole (sequence, head) chains = {head_tokens} head-tokens "
                       f"({rows} of {B} batch rows, all {H} heads), fp64 token loop, "
-                      f"{dt:.2f} s wall"}
+                      f"{dt:.2f} s wall",
+            "value_1thread": 2 * seq_len / dt1,
+            "sample_1thread": f"chains (0,0), (0,1) = {2 * seq_len} head-tokens on one thread, "
+                              f"{dt1:.2f} s wall"}
 
 
 def main():
@@ -113,6 +135,8 @@ def main():
     ap.add_argument("--segment-chunks", default="auto",
                     help="segmented form: 'auto' (used only for workloads with few chains), "
                          "'off', or a segment length in 16-token chunks")
+    ap.add_argument("--flush-cache", action="store_true",
+                    help="read a 512 MiB buffer before every launch (outside its timing)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="before warm-up, run one plain device-to-device copy of this many "
                          "bytes (untimed), as a known-size reference for HBM byte counters")
@@ -143,6 +167,21 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    # context: a plain device-to-device copy of 1 GiB (read + write), best of 3
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    best = None
+    for _ in range(4):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    copy_gbs = 2 * (1 << 30) / (best / 1e3) / 1e9
+    del src, dst
+    flush = torch.ones(512 << 20, dtype=torch.uint8, device="cuda") if args.flush_cache else None
 
     if args.segment_chunks == "auto":
         seg = kda.auto_segment_chunks(x.num_seqs * H, T)
@@ -157,6 +196,8 @@ def main():
                 check_cu_seqlens=False, segment_chunks=seg)
 
     for _ in range(args.warmup):
+        if flush is not None:
+            flush.max()
         step()
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
@@ -167,13 +208,16 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s, e in ev:
+        if flush is not None:
+            flush.max()
         s.record(stream)
         step()
         e.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     launch_ms = [s.elapsed_time(e) for s, e in ev]
-    ms_per_step = wall * 1e3 / args.steps
+    # with cache flushes in between, the wall clock would count them: use the launches
+    ms_per_step = sum(launch_ms) / len(launch_ms) if flush is not None else wall * 1e3 / args.steps
     head_tokens = B * T * H
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr,
           flush=True)
@@ -183,9 +227,12 @@ def main():
     achieved = launch_bytes / avg_launch_s / 1e9
     kernel = "mfma (segmented)" if seg else kda.fwd_kernel(T, x.cu_seqlens is not None)
     traffic = stored_traffic(args.workload, kernel)
+    flops = head_tokens * FLOPS_PER_HEAD_TOKEN
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel_ms": round(avg_launch_s * 1e3, 4), "bytes_per_launch": launch_bytes}
+                "kernel_ms": round(avg_launch_s * 1e3, 4), "bytes_per_launch": launch_bytes,
+                "flops_per_launch": round(flops),
+                "mfma_frac": round(flops / avg_launch_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
 
     result = {
         "metric": "KDA fwd head-tokens/sec (K=V=128); % of HBM/MFMA roofline",
@@ -207,6 +254,8 @@ def main():
                    "segment_chunks": seg,
                    "kernel": kernel},
         "roofline": roofline,
+        "copy_gbs": round(copy_gbs, 1),
+        "cache_flushed": flush is not None,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
