@@ -136,6 +136,7 @@ kda_status check_args(const void *q, const void *k, const void *v, const void *g
     // (lower_bound page, "Conversion to the Gate Scale Factor").
     p.gate_scale = static_cast<float>(lower_bound * kLog2e);
     p.inverse = kda::inverse_from_env();
+    p.sigmoid = kda::sigmoid_from_env();
     c->chains = chains;
     return KDA_OK;
 }
@@ -275,6 +276,14 @@ hipError_t launch_forward(const FwdParams &p, hipStream_t stream)
     case kKernelRecurrent: return launch_decode(p, stream);
     default: return launch_chunk_mfma(p, stream);
     }
+}
+
+// KDA_SIGMOID=tanh selects the rational-tanh form of the logistic function in
+// the MFMA kernel's gate (an ablation of the pages' choice); read at every call.
+int sigmoid_from_env()
+{
+    const char *e = std::getenv("KDA_SIGMOID");
+    return e && std::strcmp(e, "tanh") == 0 ? kSigmoidTanh : kSigmoidExp;
 }
 
 // KDA_INVERSE=neumann selects the fp16 Neumann-product inverse in the MFMA

@@ -287,6 +287,19 @@ __device__ __forceinline__ void row_products(float x, float fh, float fo, float 
 // gate waves
 // ---------------------------------------------------------------------------
 
+// tanh(y) ~ y P(y^2) / Q(y^2) on |y| <= 9 (beyond, tanh = 1 to 2^-23), P and Q
+// of degree 4 in y^2 with P(0) = Q(0) = 1: a rational fit of tanh by weighted
+// least squares on the relative error (gated_delta_rule_36_amd/fit_tanh.py);
+// in fp32, Horner order, the error is about 3e-7 on the whole line.  Used
+// by the tanh form of the logistic function, sigma(x) = 1/2 + tanh(x/2)/2,
+// which needs no exponential (the pages' sigmoid_tanh_approx; gfx950 has no
+// tanh instruction).
+constexpr float kTanhClamp = 9.0f;
+constexpr float kTanhP1 = 0.13381032645702362f, kTanhP2 = 0.0034955963492393494f,
+                kTanhP3 = 2.0609206330846064e-05f, kTanhP4 = 1.3354815919797147e-08f;
+constexpr float kTanhQ1 = 0.4671434760093689f, kTanhQ2 = 0.02587701380252838f,
+                kTanhQ3 = 0.0003285647835582495f, kTanhQ4 = 7.776625352562405e-07f;
+
 // Plain load (the beta logits): the compiler tracks it and waits (s_waitcnt
 // vmcnt) right before the first use of the register.
 __device__ __forceinline__ uint32_t gload_u16(const char *p)
@@ -369,6 +382,8 @@ struct GateWave {
     float bias_neg;  // head_neg * dt_bias[h][16 gc16 + l16]
     float grp_hi;   // (g4 >= 2)
     float grp_odd;  // (g4 odd)
+    // tanh form: y = x / 2 = head_y g + bias_y; a = gs_half (1 + tanh y)
+    float head_y, bias_y, gs_half;
 
     __device__ int chunk_len(int x) const { return x < n_full ? C : tail; }
 
@@ -376,14 +391,15 @@ struct GateWave {
     // 16 channels.  FULL: all 16 rows of the chunk lie in the sequence.
     // o3, o5: offsets of chunk x's stage slot and of its Qt / Kbar ring slot
     // (x mod 3 and x mod 5 slots, kept as running offsets by the caller).
+    template <int SIG>
     __device__ void gate_stage(int x, uint32_t o3, uint32_t o5) const
     {
         if (x < n_full)
-            gate_rows<true>(x, o3, o5);
+            gate_rows<true, SIG>(x, o3, o5);
         else
-            gate_rows<false>(x, o3, o5);
+            gate_rows<false, SIG>(x, o3, o5);
     }
-    template <bool FULL>
+    template <bool FULL, int SIG>
     __device__ void gate_rows(int x, uint32_t o3, uint32_t o5) const
     {
         const int len = FULL ? C : tail;
@@ -403,9 +419,18 @@ struct GateWave {
         float al[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float e = exp2_f32(fmaf(cg[i], head_neg, bias_neg));
-            const float s = __builtin_amdgcn_rcpf(1.0f + e);
-            const float a = exp2_f32(p.gate_scale * s);
+            float a;
+            if constexpr (SIG == kSigmoidTanh) {
+                const float y = __builtin_amdgcn_fmed3f(fmaf(cg[i], head_y, bias_y), -kTanhClamp, kTanhClamp);
+                const float u = y * y;
+                const float pn = fmaf(fmaf(fmaf(fmaf(kTanhP4, u, kTanhP3), u, kTanhP2), u, kTanhP1), u, 1.0f);
+                const float qd = fmaf(fmaf(fmaf(fmaf(kTanhQ4, u, kTanhQ3), u, kTanhQ2), u, kTanhQ1), u, 1.0f);
+                a = exp2_f32(fmaf(gs_half, y * pn * __builtin_amdgcn_rcpf(qd), gs_half));
+            } else {
+                const float e = exp2_f32(fmaf(cg[i], head_neg, bias_neg));
+                const float s = __builtin_amdgcn_rcpf(1.0f + e);
+                a = exp2_f32(p.gate_scale * s);
+            }
             al[i] = (FULL || 4 * g4 + i < len) ? a : 1.0f;
         }
         // products within the 4-token group, then across the 4 groups
@@ -804,7 +829,8 @@ __device__ __forceinline__ void state_loop(StateWave &sw, int n_iter, int nc)
 // output pass, kChunkState for the segment end states, kChunkTransition for
 // the segment transition matrices).  One mode per kernel: with several state
 // loops in one kernel the compiler runs out of registers.
-template <int MODE, int INV>
+// INV: the inverse (Inverse); SIG: the gate's logistic function (Sigmoid).
+template <int MODE, int INV, int SIG = kSigmoidExp>
 __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
 {
     __shared__ Shared sh;
@@ -1015,6 +1041,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
     const float head_mult = p.A_log ? expf(p.A_log[h]) : 1.0f;
     gw.head_neg = -head_mult * kLog2eF;
     gw.bias_neg = p.dt_bias ? gw.head_neg * p.dt_bias[h * D + 16 * gc16 + l16] : 0.f;
+    gw.head_y = 0.5f * head_mult;  // x / 2 = exp(A_log) (g + dt_bias) / 2
+    gw.bias_y = p.dt_bias ? gw.head_y * p.dt_bias[h * D + 16 * gc16 + l16] : 0.f;
+    gw.gs_half = 0.5f * p.gate_scale;
     gw.grp_hi = g4 >= 2 ? 1.0f : 0.0f;
     gw.grp_odd = (g4 & 1) ? 1.0f : 0.0f;
     if (n_iter == 0)
@@ -1050,7 +1079,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
             ld.issue();
             ld.advance(nc);
         }
-        gw.gate_stage(it, o3, o5);
+        gw.gate_stage<SIG>(it, o3, o5);
         o3 = o3 == 2 * (3 * kTile) ? 0 : o3 + 3 * kTile;
         o5 = o5 == 4 * kTile ? 0 : o5 + kTile;
         wait_vmem<2>();  // chunk it + 1
@@ -1075,6 +1104,9 @@ hipError_t launch_chunk_mfma(const FwdParams &p, hipStream_t stream)
         kernel = p.phase == kPhaseMapB   ? reinterpret_cast<const void *>(&chunk_mfma_kernel<kChunkState, kInverseSubst>)
                  : p.phase == kPhaseMapM ? reinterpret_cast<const void *>(&chunk_mfma_kernel<kChunkTransition, kInverseSubst>)
                                          : reinterpret_cast<const void *>(&chunk_mfma_kernel<kChunkFull, kInverseSubst>);
+    // the tanh-form gate is built for whole chains with the default inverse
+    if (p.sigmoid == kSigmoidTanh && p.phase == kPhaseWhole && p.inverse == kInverseSubst)
+        kernel = reinterpret_cast<const void *>(&chunk_mfma_kernel<kChunkFull, kInverseSubst, kSigmoidTanh>);
     FwdParams args = p;
     void *argv[] = {&args};
     return hipLaunchKernel(kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), argv, 0, stream);

@@ -15,6 +15,10 @@ enum Phase : int { kPhaseWhole = 0, kPhaseMapB = 1, kPhaseMapM = 2, kPhaseOut = 
 // How the MFMA kernel forms T = (I + A)^-1: fp32 forward substitution (the
 // default) or the fp16 Neumann product (KDA_INVERSE=neumann; an ablation).
 enum Inverse : int { kInverseSubst = 0, kInverseNeumann = 1 };
+// How the MFMA kernel's gate evaluates the logistic function: 1/(1 + 2^-x')
+// with the hardware exp2 and rcp (the default), or 1/2 + tanh(x/2)/2 with a
+// rational tanh (KDA_SIGMOID=tanh; an ablation, whole-chain calls only).
+enum Sigmoid : int { kSigmoidExp = 0, kSigmoidTanh = 1 };
 
 // Everything a launch needs.  Pointers are device pointers; sizes were
 // validated by the front end.
@@ -32,6 +36,7 @@ struct FwdParams {
     float scale;                           // read-out scale
     float gate_scale;                      // lower_bound * log2(e), in fp32
     int inverse = kInverseSubst;           // Inverse (MFMA kernel)
+    int sigmoid = kSigmoidExp;             // Sigmoid (MFMA kernel, whole chains)
 
     // Intra-sequence scan (kda_fwd_scan).  Every chain is cut into segments
     // of seg_chunks chunks; segment s maps its start state S to M_s S + b_s
@@ -55,6 +60,9 @@ hipError_t launch_forward(const FwdParams &p, hipStream_t stream);
 // The inverse method the environment selects (KDA_INVERSE=neumann), read at
 // every call.
 int inverse_from_env();
+// The sigmoid form the environment selects (KDA_SIGMOID=tanh), read at every
+// call.
+int sigmoid_from_env();
 
 // Enqueue the segmented form: map (phase 1), combine, output (phase 3).
 // p.seg_chunks, p.n_seg, p.seg_b and p.seg_m must be set.

@@ -55,6 +55,9 @@ def test_library_has_gfx950_code_and_no_oracle():
 
 FAKE = [ctypes.create_string_buffer(64 + 16) for _ in range(12)]
 ADDR = [(ctypes.addressof(b) + 15) & ~15 for b in FAKE]  # 16-byte aligned, like allocator memory
+# a whole fp32 state (H = 1) of its own, so that a state span cannot overlap the other dummies
+STATE_BUF = ctypes.create_string_buffer(128 * 128 * 4 + 32)
+STATE_ADDR = (ctypes.addressof(STATE_BUF) + 15) & ~15
 
 
 def call(**over):
@@ -105,7 +108,7 @@ def call(**over):
     (dict(beta=ADDR[4] + 1), _lib.KDA_ERR_ALIGNMENT),
     (dict(dt_bias=ADDR[7] + 2), _lib.KDA_ERR_ALIGNMENT),
     (dict(init=ADDR[8] + 8, init_dtype=1), _lib.KDA_ERR_ALIGNMENT),
-    (dict(final=ADDR[10] + 8, final_dtype=2), _lib.KDA_ERR_ALIGNMENT),
+    (dict(final=STATE_ADDR + 8, final_dtype=2), _lib.KDA_ERR_ALIGNMENT),
     (dict(cu=ADDR[9] + 4, num_seqs=0), _lib.KDA_ERR_ALIGNMENT),
 ])
 def test_argument_errors_are_reported_before_launch(over, code):
@@ -247,3 +250,20 @@ def test_binding_rejects_host_tensors():
 def test_binding_rejects_non_tensors():
     with pytest.raises(TypeError):
         kda.fwd(**_cpu_args(q=[1, 2, 3]))
+
+
+def test_rational_tanh_constants_match_their_fit():
+    """The kernel's rational-tanh coefficients are the ones fit_tanh.py
+    produces, and their fp32 evaluation stays within 5e-7 of tanh."""
+    import re
+    import numpy as np
+    from gated_delta_rule_36_amd import fit_tanh
+    src = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                            "gated_delta_rule_36_amd", "csrc", "kda_chunk_mfma.hip")).read()
+    consts = {m.group(1): float(m.group(2)) for m in re.finditer(r"kTanh([PQ]\d) = ([0-9.e+-]+)f", src)}
+    p, q = fit_tanh.fit()
+    for i in range(1, 5):
+        assert np.float32(consts[f"P{i}"]) == p[i] and np.float32(consts[f"Q{i}"]) == q[i]
+    assert p[0] == 1.0 and q[0] == 1.0
+    ys = np.linspace(-20, 20, 100001)
+    assert float(np.abs(fit_tanh.tanh32(ys, p, q) - np.tanh(ys)).max()) < 5e-7

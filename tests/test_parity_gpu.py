@@ -608,3 +608,54 @@ def test_kernel_choice_is_read_per_call(monkeypatch):
     assert not np.array_equal(f_rec, f_mf)
     assert_close("recurrent vs chunked out", o_rec, o_mf)
     assert_close("recurrent vs chunked final", f_rec, f_mf)
+
+
+# --------------------------------------------------------------------------
+# the tanh form of the gate's logistic function (KDA_SIGMOID=tanh): an
+# ablation of the pages' choice, on whole-chain calls of the chunked kernel
+# --------------------------------------------------------------------------
+
+@pytest.fixture
+def tanh_sigmoid(monkeypatch):
+    monkeypatch.setenv("KDA_SIGMOID", "tanh")
+    monkeypatch.setenv("KDA_KERNEL", "mfma")  # short calls would take the recurrent kernel
+
+
+def test_tanh_sigmoid_small_workload(tanh_sigmoid):
+    print("[case] tanh sigmoid small workload", flush=True)
+    check_full("tanh small", synth.workload("small_b2_t128_h8", device="cuda"), torch.float32)
+
+
+@pytest.mark.parametrize("T", [1, 17, 100])
+def test_tanh_sigmoid_ragged(tanh_sigmoid, T):
+    print(f"[case] tanh sigmoid T={T}", flush=True)
+    x = synth.make_inputs(2, T, 3, lower_bound=-5.0, seed=400 + T, init_dtype=torch.float32,
+                          device="cuda")
+    check_full(f"tanh T={T}", x, torch.float32)
+
+
+def test_tanh_sigmoid_gate_extremes(tanh_sigmoid):
+    """Saturated gates (g = +-100) hit the clamp of the rational tanh."""
+    x = synth.make_inputs(2, 96, 4, lower_bound=-5.0, seed=401, init_dtype=torch.float32,
+                          device="cuda")
+    x.g.fill_(100.0)
+    print("[case] tanh max decay", flush=True)
+    check_full("tanh max decay", x, torch.float32)
+    y = synth.make_inputs(1, 64, 2, lower_bound=-5.0, seed=402, init_dtype=torch.float32,
+                          device="cuda")
+    y.g.fill_(-100.0)
+    y.beta.fill_(8.0)
+    print("[case] tanh min decay, large beta", flush=True)
+    check_full("tanh min decay", y, torch.float32)
+
+
+def test_sigmoid_choice_is_read_per_call(monkeypatch):
+    x = synth.make_inputs(1, 64, 2, lower_bound=-5.0, seed=403, device="cuda")
+    o_exp, _ = run_gpu(x)
+    monkeypatch.setenv("KDA_SIGMOID", "tanh")
+    o_tanh, _ = run_gpu(x)
+    monkeypatch.delenv("KDA_SIGMOID")
+    o_exp2, _ = run_gpu(x)
+    assert np.array_equal(o_exp, o_exp2)
+    assert not np.array_equal(o_exp, o_tanh)
+    assert_close("tanh vs exp2 sigmoid", o_tanh, o_exp)
