@@ -745,10 +745,10 @@ struct StateWave {
     // Y, no output); kChunkTransition: the state with v ignored (U = -W S),
     // which carries an identity start to the range's transition matrix.
     template <int MODE>
-    __device__ void chunk(int x)
+    __device__ void chunk(int x, uint32_t o5)
     {
         constexpr bool kOut = MODE == kChunkFull;
-        const uint32_t s2 = x & 1, s4 = x & 3, s5 = x % 5;
+        const uint32_t s2 = x & 1, s4 = x & 3;
         const int len = x < n_full ? C : tail;
 
         // X = W S (lane (vcol, g4): rows 4g4..4g4+3) and Y^T = S^T Qt^T (lane
@@ -758,7 +758,7 @@ struct StateWave {
         // 32kt + 4g4 + e (e < 4) and 32kt + 16 + 4g4 + (e - 4) (e >= 4), which
         // is exactly what this lane's accumulators of tiles 2kt, 2kt+1 hold
         // and what chunk 4 kt + g4 of a W row holds.
-        const uint32_t aw = slot_base(rd_w + s2 * kTileW), aq = slot_base(rd_q + s5 * kTile);
+        const uint32_t aw = slot_base(rd_w + s2 * kTileW), aq = slot_base(rd_q + o5);
         f32x4_t X[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         f32x4_t Y[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -804,7 +804,7 @@ struct StateWave {
         }
 
         // S <- diag(Gamma_C) S + Kbar^T U
-        const uint32_t ag = slot_base(rd_g + s5 * kTileGam), ak = slot_base(rd_k + s5 * kTile);
+        const uint32_t ag = slot_base(rd_g + (o5 >> 3)), ak = slot_base(rd_k + o5);
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
             const f32x4_t gc = lds_ld<f32x4_t>(ag + 64 * mt);
@@ -818,9 +818,12 @@ struct StateWave {
 template <int MODE>
 __device__ __forceinline__ void state_loop(StateWave &sw, int n_iter, int nc)
 {
+    uint32_t o5 = 0;  // chunk x's Qt / Kbar ring slot (x mod 5), as a running offset
     for (int it = 0; it < n_iter; ++it) {
-        if (it >= kStages && it - kStages < nc)
-            sw.chunk<MODE>(it - kStages);
+        if (it >= kStages && it - kStages < nc) {
+            sw.chunk<MODE>(it - kStages, o5);
+            o5 = o5 == 4 * kTile ? 0 : o5 + kTile;
+        }
         lds_barrier();
     }
 }
