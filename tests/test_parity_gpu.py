@@ -659,3 +659,37 @@ def test_sigmoid_choice_is_read_per_call(monkeypatch):
     assert np.array_equal(o_exp, o_exp2)
     assert not np.array_equal(o_exp, o_tanh)
     assert_close("tanh vs exp2 sigmoid", o_tanh, o_exp)
+
+
+# --------------------------------------------------------------------------
+# more chains than compute units, and the write-free degenerate case, on
+# both kernels
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kernel", ["mfma", "recurrent"])
+def test_many_chains_sampled(kernel, monkeypatch):
+    """2048 chains (8 per compute unit) of 40 tokens: grids far larger than
+    the GPU, with a ragged last chunk; sampled chains against the oracle."""
+    monkeypatch.setenv("KDA_KERNEL", kernel)
+    print(f"[case] many chains kernel={kernel}", flush=True)
+    x = synth.make_inputs(2, 40, 1024, lower_bound=-5.0, seed=500, init_dtype=torch.float32,
+                          device="cuda")
+    o, f = run_gpu(x, torch.float32)
+    chains = [(0, 0), (0, 511), (1, 3), (1, 1023)]
+    for (n, h), (ro, rf) in zip(chains, oracle_of(x, chains=chains)):
+        assert_close(f"many chains {kernel} out[{n},:,{h}]", o[n, :, h], ro)
+        assert_close(f"many chains {kernel} final[{n},{h}]", f[n, h], rf)
+    assert np.isfinite(o).all() and np.isfinite(f).all()
+
+
+@pytest.mark.parametrize("kernel", ["mfma", "recurrent"])
+def test_beta_zero_is_pure_decay(kernel, monkeypatch):
+    """beta logits of -100 (beta = 3.7e-44, i.e. no writes): the state only
+    decays, final = diag(Gamma_L) S0 and o_t = scale (diag(Gamma_t) S0)^T q_t;
+    the oracle computes the same closed form token by token."""
+    monkeypatch.setenv("KDA_KERNEL", kernel)
+    print(f"[case] beta = 0 kernel={kernel}", flush=True)
+    x = synth.make_inputs(2, 37, 3, lower_bound=-2.0, seed=501, init_dtype=torch.float32,
+                          device="cuda")
+    x.beta.fill_(-100.0)
+    check_full(f"beta zero {kernel}", x, torch.float32)
