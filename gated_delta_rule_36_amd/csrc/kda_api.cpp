@@ -250,12 +250,14 @@ extern "C" const char *kda_status_string(kda_status status)
 extern "C" int kda_abi_version(void) { return KDA_ABI_VERSION; }
 
 namespace kda {
-// Kernel choice, read at every call.  By default calls without cu_seqlens
-// and with at most kDecodeMaxTokens tokens per sequence (decode-shaped: the
-// state traffic dominates) take the recurrent kernel, everything else the
-// chunked MFMA kernel.  KDA_KERNEL=mfma, =recurrent or =simt (the plain fp32
-// chunked kernel, for cross-checks) forces one for every call.
-enum KernelChoice { kKernelMfma, kKernelRecurrent, kKernelSimt };
+// Kernel choice, read at every call.  Calls without cu_seqlens of at most
+// one chunk per sequence are decode-shaped (the state traffic dominates): up
+// to kRecurrentMaxTokens tokens they take the recurrent kernel, up to 16 the
+// single-chunk kernel; everything else takes the pipelined chunked kernel.
+// KDA_KERNEL=mfma, =recurrent, =single (calls it can take; others fall back
+// to mfma) or =simt (the plain fp32 chunked kernel, for cross-checks) forces
+// the choice for every call.
+enum KernelChoice { kKernelMfma, kKernelRecurrent, kKernelSingle, kKernelSimt };
 
 static KernelChoice kernel_choice(int64_t T, bool varlen)
 {
@@ -266,7 +268,12 @@ static KernelChoice kernel_choice(int64_t T, bool varlen)
         return kKernelRecurrent;
     if (e && std::strcmp(e, "mfma") == 0)
         return kKernelMfma;
-    return !varlen && T <= kDecodeMaxTokens ? kKernelRecurrent : kKernelMfma;
+    const bool one_chunk = !varlen && T <= kChunk;  // what the single-chunk kernel takes
+    if (e && std::strcmp(e, "single") == 0)
+        return one_chunk ? kKernelSingle : kKernelMfma;
+    if (!varlen && T <= kRecurrentMaxTokens)
+        return kKernelRecurrent;
+    return one_chunk ? kKernelSingle : kKernelMfma;
 }
 
 hipError_t launch_forward(const FwdParams &p, hipStream_t stream)
@@ -274,6 +281,7 @@ hipError_t launch_forward(const FwdParams &p, hipStream_t stream)
     switch (kernel_choice(p.T, p.cu_seqlens != nullptr)) {
     case kKernelSimt: return launch_chunk_simt(p, stream);
     case kKernelRecurrent: return launch_decode(p, stream);
+    case kKernelSingle: return launch_chunk_single(p, stream);
     default: return launch_chunk_mfma(p, stream);
     }
 }
@@ -320,6 +328,7 @@ extern "C" const char *kda_fwd_kernel(int64_t T, int varlen)
     switch (kda::kernel_choice(T, varlen != 0)) {
     case kda::kKernelSimt: return "simt";
     case kda::kKernelRecurrent: return "recurrent";
+    case kda::kKernelSingle: return "single";
     default: return "mfma";
     }
 }

@@ -139,7 +139,7 @@ __device__ __forceinline__ uint32_t row32_lane(int l16, int g4)
 
 // Ring buffers between the stages; a tile written for chunk x lives in slot
 // x mod (its ring size), which is sized to outlive its last reader.
-struct __align__(16) Shared {
+struct __align__(16) SharedPipe {
     uint16_t kt_col[4][D][C];  // Kt, channel-major; read by A and WY
     uint16_t kh_col[2][D][C];  // Kh, channel-major; read by A and P
     uint16_t qt_col[5][D][C];  // Qt (scale folded in), channel-major; read by P and the state stage
@@ -156,14 +156,63 @@ struct __align__(16) Shared {
     uint16_t stage[3][3][C][D];  // q, k, g as loaded (DMA), token-major; read by the gate stage
 };
 
-// Byte offsets of the rings within Shared, and the bytes of one ring slot.
-constexpr uint32_t kOffKt = offsetof(Shared, kt_col), kOffKh = offsetof(Shared, kh_col);
-constexpr uint32_t kOffQt = offsetof(Shared, qt_col), kOffV = offsetof(Shared, v_row);
-constexpr uint32_t kOffKb = offsetof(Shared, kb_col), kOffGam = offsetof(Shared, gam_c);
-constexpr uint32_t kOffBeta = offsetof(Shared, beta), kOffA = offsetof(Shared, amat);
-constexpr uint32_t kOffP = offsetof(Shared, pmat), kOffThi = offsetof(Shared, tb_hi);
-constexpr uint32_t kOffTlo = offsetof(Shared, tb_lo), kOffW = offsetof(Shared, w_row);
-constexpr uint32_t kOffU = offsetof(Shared, ut), kOffStage = offsetof(Shared, stage);
+// The same tiles with one slot each, for a single chunk per workgroup (the
+// single-chunk kernel below): W and U~ are written only after the gate stage
+// has read the staging tiles, so they share that space.
+struct __align__(16) SharedSingle {
+    uint16_t kt_col[1][D][C];
+    uint16_t kh_col[1][D][C];
+    uint16_t qt_col[1][D][C];
+    uint16_t v_row[1][C][D];
+    uint16_t kb_col[1][D][C];
+    float gam_c[1][D];
+    float beta[1][C];
+    float amat[1][C][AP];
+    uint16_t pmat[1][C][C];
+    uint16_t tb_hi[1][C][C];
+    uint16_t tb_lo[1][C][C];
+    union {
+        uint16_t stage[1][3][C][D];
+        struct {
+            uint16_t w_row[1][C][kWPitch];
+            float ut[1][D][C];
+        } wu;
+    };
+};
+
+// Byte offsets of the tiles within a layout's shared block.
+struct PipeLayout {
+    static constexpr uint32_t kOffKt = offsetof(SharedPipe, kt_col), kOffKh = offsetof(SharedPipe, kh_col);
+    static constexpr uint32_t kOffQt = offsetof(SharedPipe, qt_col), kOffV = offsetof(SharedPipe, v_row);
+    static constexpr uint32_t kOffKb = offsetof(SharedPipe, kb_col), kOffGam = offsetof(SharedPipe, gam_c);
+    static constexpr uint32_t kOffBeta = offsetof(SharedPipe, beta), kOffA = offsetof(SharedPipe, amat);
+    static constexpr uint32_t kOffP = offsetof(SharedPipe, pmat), kOffThi = offsetof(SharedPipe, tb_hi);
+    static constexpr uint32_t kOffTlo = offsetof(SharedPipe, tb_lo), kOffW = offsetof(SharedPipe, w_row);
+    static constexpr uint32_t kOffU = offsetof(SharedPipe, ut), kOffStage = offsetof(SharedPipe, stage);
+};
+struct SingleLayout {
+    static constexpr uint32_t kOffKt = offsetof(SharedSingle, kt_col), kOffKh = offsetof(SharedSingle, kh_col);
+    static constexpr uint32_t kOffQt = offsetof(SharedSingle, qt_col), kOffV = offsetof(SharedSingle, v_row);
+    static constexpr uint32_t kOffKb = offsetof(SharedSingle, kb_col), kOffGam = offsetof(SharedSingle, gam_c);
+    static constexpr uint32_t kOffBeta = offsetof(SharedSingle, beta), kOffA = offsetof(SharedSingle, amat);
+    static constexpr uint32_t kOffP = offsetof(SharedSingle, pmat), kOffThi = offsetof(SharedSingle, tb_hi);
+    static constexpr uint32_t kOffTlo = offsetof(SharedSingle, tb_lo), kOffW = offsetof(SharedSingle, wu.w_row);
+    static constexpr uint32_t kOffU = offsetof(SharedSingle, wu.ut), kOffStage = offsetof(SharedSingle, stage);
+};
+// The stage structs below take the layout as a template parameter and see its
+// offsets under these names.
+#define KDA_LAYOUT_OFFSETS(L)                                                                     \
+    static constexpr uint32_t kOffKt = L::kOffKt, kOffKh = L::kOffKh, kOffQt = L::kOffQt;         \
+    static constexpr uint32_t kOffV = L::kOffV, kOffKb = L::kOffKb, kOffGam = L::kOffGam;         \
+    static constexpr uint32_t kOffBeta = L::kOffBeta, kOffA = L::kOffA, kOffP = L::kOffP;         \
+    static constexpr uint32_t kOffThi = L::kOffThi, kOffTlo = L::kOffTlo, kOffW = L::kOffW;       \
+    static constexpr uint32_t kOffU = L::kOffU, kOffStage = L::kOffStage;
+// The pipelined kernel's offsets, for its own address set-up.
+constexpr uint32_t kOffKt = PipeLayout::kOffKt, kOffKh = PipeLayout::kOffKh, kOffQt = PipeLayout::kOffQt;
+constexpr uint32_t kOffV = PipeLayout::kOffV, kOffKb = PipeLayout::kOffKb, kOffGam = PipeLayout::kOffGam;
+constexpr uint32_t kOffBeta = PipeLayout::kOffBeta, kOffA = PipeLayout::kOffA, kOffP = PipeLayout::kOffP;
+constexpr uint32_t kOffThi = PipeLayout::kOffThi, kOffTlo = PipeLayout::kOffTlo, kOffW = PipeLayout::kOffW;
+constexpr uint32_t kOffU = PipeLayout::kOffU, kOffStage = PipeLayout::kOffStage;
 constexpr uint32_t kTile = D * C * 2;          // bf16 [D][C] or [C][D] tile
 constexpr uint32_t kTileW = C * kWPitch * 2;   // W tile
 constexpr uint32_t kTileU = D * C * 4;         // U~ tile (fp32)
@@ -368,7 +417,9 @@ struct Loader {
     }
 };
 
+template <class L>
 struct GateWave {
+    KDA_LAYOUT_OFFSETS(L)
     const FwdParams &p;
     int gc16;  // 0..7: channels 16 gc16 .. 16 gc16 + 15, wave-uniform
     int lane, l16, g4;
@@ -466,7 +517,9 @@ struct GateWave {
 // solve waves
 // ---------------------------------------------------------------------------
 
+template <class L>
 struct SolveWave {
+    KDA_LAYOUT_OFFSETS(L)
     int pw;  // 0..3, wave-uniform
     int l16, g4;
     // LDS addresses (ring slot 0, without the ring's offset) of this lane's
@@ -674,7 +727,9 @@ enum ChunkMode : int { kChunkFull = 0, kChunkState = 1, kChunkTransition = 2 };
 // kDstFp32T: fp32, untransposed ([K][V]: element [k][v] = S[k][v]).
 enum StateDst : int { kDstNone = 0, kDstFp32 = 2, kDstBf16 = 3, kDstFp32T = 4 };
 
+template <class L>
 struct StateWave {
+    KDA_LAYOUT_OFFSETS(L)
     const FwdParams &p;
     int w, lane, l16, g4;
     int n_full, tail;          // full chunks of the range; length of a partial last chunk
@@ -815,13 +870,13 @@ struct StateWave {
     }
 };
 
-template <int MODE>
-__device__ __forceinline__ void state_loop(StateWave &sw, int n_iter, int nc)
+template <int MODE, class L>
+__device__ __forceinline__ void state_loop(StateWave<L> &sw, int n_iter, int nc)
 {
     uint32_t o5 = 0;  // chunk x's Qt / Kbar ring slot (x mod 5), as a running offset
     for (int it = 0; it < n_iter; ++it) {
         if (it >= kStages && it - kStages < nc) {
-            sw.chunk<MODE>(it - kStages, o5);
+            sw.template chunk<MODE>(it - kStages, o5);
             o5 = o5 == 4 * kTile ? 0 : o5 + kTile;
         }
         lds_barrier();
@@ -836,7 +891,7 @@ __device__ __forceinline__ void state_loop(StateWave &sw, int n_iter, int nc)
 template <int MODE, int INV, int SIG = kSigmoidExp>
 __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
 {
-    __shared__ Shared sh;
+    __shared__ SharedPipe sh;
     // Block -> chain (and, in the segmented form, segment).  The grid is
     // below 2^31 blocks (checked on the host), so 32-bit arithmetic suffices;
     // readfirstlane keeps these wave-uniform values in scalar registers.
@@ -913,7 +968,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
     const uint32_t sh0 = lds_addr(&sh);
 
     if (wave < 4) {
-        StateWave sw{p, wave, lane, l16, g4, n_full, tail,
+        StateWave<PipeLayout> sw{p, wave, lane, l16, g4, n_full, tail,
                                   reinterpret_cast<char *>(p.out + first * D + 32 * wave),
                                   C * tok_bytes,
                                   static_cast<uint32_t>(l16 * tok_bytes + 16 * g4),
@@ -928,7 +983,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
         sw.load_state(src, src_ptr, src_slab);
         if (n_iter > 0)
             lds_barrier();  // the gate waves' first loads are in LDS
-        state_loop<MODE>(sw, n_iter, nc);
+        state_loop<MODE, PipeLayout>(sw, n_iter, nc);
         sw.store_state(dst, dst_ptr, dst_slab);
         return;
     }
@@ -936,7 +991,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
     if (wave >= 12) {
         const int pw = wave - 12;
         const int j0 = 8 * (pw - 2) + 2 * g4;  // the solve waves' column pair
-        const SolveWave sv{pw, l16, g4,
+        const SolveWave<PipeLayout> sv{pw, l16, g4,
                            sh0 + tok_lane(l16, g4),
                            sh0 + row16_lane(l16, g4),
                            sh0 + kOffA + 4 * (4 * g4 * AP + l16),
@@ -1037,7 +1092,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
 
     // gate waves
     const int gc16 = wave - 4;
-    GateWave gw{p, gc16, lane, l16, g4, n_full, tail,
+    GateWave<PipeLayout> gw{p, gc16, lane, l16, g4, n_full, tail,
                 sh0 + kOffStage + chan_lane(16 * gc16, l16, g4),
                 sh0 + 512 * gc16 + row16_lane(l16, g4),
                 sh0 + kOffGam + 4 * (16 * gc16 + l16)};
@@ -1092,6 +1147,126 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
     wait_vmem<0>();
 }
 
+// One chunk per workgroup: the stages of the pipelined kernel run in order
+// for a single chunk of at most 16 tokens, by 4 waves with the tiles of
+// SharedSingle (36 KiB, so four chains share a compute unit), one barrier
+// between stages.  For decode-shaped calls (T <= 16, no cu_seqlens): the
+// state's loads overlap the loads, gate and solve of the chunk, and four
+// workgroups per compute unit overlap one another's state traffic.  Wave w
+// loads tensor w (q, k, g into the staging tiles, v into the V tile), takes
+// channel groups 2w and 2w + 1 of the gate stage, the solve roles of solve
+// wave w (A for w = 0, P for 1, T for 2 and 3, then WY for channels / value
+// columns 32w ..) and value columns 32w .. of the state.
+template <int SIG>
+__global__ __launch_bounds__(256, 4) void chunk_single_kernel(FwdParams p)
+{
+    using SL = SingleLayout;
+    __shared__ SharedSingle sh;
+    const int chain = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x));
+    const int H = static_cast<int>(p.H);
+    const int64_t n = chain / H, h = chain - (chain / H) * H;
+    int64_t t_begin, t_end, row;
+    chain_segment(p, n, &t_begin, &t_end, &row);
+    const int src = p.init_state ? (p.init_kind == kStateBf16 ? kSrcBf16 : kSrcFp32) : kSrcZero;
+    const int dst = p.final_state ? (p.final_kind == kStateBf16 ? kDstBf16 : kDstFp32) : kDstNone;
+    const int64_t slab = int64_t(chain) * D * D;
+    // the host sends only calls of at most one chunk per sequence
+    const int len_seq = static_cast<int>(t_end - t_begin);
+    const int n_full = len_seq / C, tail = len_seq % C;
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int64_t tok_bytes = p.H * D * 2;
+    const int64_t first = (row * p.T + t_begin) * p.H + h;
+    const uint32_t sh0 = lds_addr(&sh);
+
+    StateWave<SL> sw{p, wave, lane, l16, g4, n_full, tail,
+                     reinterpret_cast<char *>(p.out + first * D + 32 * wave),
+                     C * tok_bytes,
+                     static_cast<uint32_t>(l16 * tok_bytes + 16 * g4),
+                     sh0 + SL::kOffQt + tok_lane(l16, g4),
+                     sh0 + SL::kOffW + 2 * kWPitch * l16 + 16 * g4,
+                     sh0 + SL::kOffU + 128 * C * wave + row32_lane(l16, g4),
+                     sh0 + SL::kOffP + row16_lane(l16, g4),
+                     sh0 + SL::kOffGam + 16 * g4,
+                     sh0 + SL::kOffKb + row16_lane(l16, g4),
+                     {}};
+    if (len_seq == 0) {  // an empty sequence passes its state through
+        sw.load_state(src, p.init_state, slab);
+        sw.store_state(dst, p.final_state, slab);
+        return;
+    }
+
+    // Loads: the chunk's rows first, then beta (wave 0) and the state, so
+    // that the wait for the rows leaves the state loads in flight.
+    Loader<4> ld;
+    ld.init((wave == 0 ? p.q : wave == 1 ? p.k : wave == 2 ? p.g : p.v) + first * D, tok_bytes, 0, lane,
+            tail, n_full, sh0 + (wave < 3 ? SL::kOffStage + wave * kTile : SL::kOffV), kTile, 1);
+    ld.issue();
+    const int pw = wave;
+    const int j0 = 8 * (pw - 2) + 2 * g4;  // the T solve's column pair (waves 2, 3)
+    const SolveWave<SL> sv{pw, l16, g4,
+                           sh0 + tok_lane(l16, g4),
+                           sh0 + row16_lane(l16, g4),
+                           sh0 + SL::kOffA + 4 * (4 * g4 * AP + l16),
+                           sh0 + SL::kOffA + 4 * AP * l16,
+                           sh0 + SL::kOffBeta + (pw == 0 ? 16 * g4 : 4 * j0),
+                           sh0 + 2 * (l16 * C + chunk16(l16, j0 >> 2) + (j0 & 3)),
+                           sh0 + SL::kOffKt + 64 * C * pw + row16_lane(l16, g4),
+                           sh0 + SL::kOffW + 2 * kWPitch * l16 + 16 * (4 * pw + g4),
+                           sh0 + SL::kOffV + chan_lane(32 * pw, l16, g4),
+                           sh0 + SL::kOffV + chan_lane(32 * pw + 16, l16, g4),
+                           sh0 + SL::kOffU + 128 * C * pw + row32_lane(l16, g4),
+                           lane, n_full, tail,
+                           reinterpret_cast<const char *>(p.beta + first),
+                           C * p.H * 2,
+                           lane < C ? static_cast<uint32_t>(lane * p.H * 2) : 0u,
+                           sh0 + SL::kOffBeta + 4 * lane,
+                           sh0 + SL::kOffBeta + 16 * g4};
+    const uint32_t logit = wave == 0 ? sv.load_beta(0) : 0u;
+    sw.load_state(src, p.init_state, slab);
+    // The 16 state loads (fp32 or bf16 initial state) come after the row
+    // loads; allowing 8 of them in flight still covers the rows.
+    if (src == kSrcFp32 || src == kSrcBf16)
+        wait_vmem<8>();
+    else
+        wait_vmem<0>();
+    if (wave == 0)
+        sv.put_beta(0, logit);
+
+    const float head_mult = p.A_log ? expf(p.A_log[h]) : 1.0f;
+    auto gate = [&](int gc16) {
+        GateWave<SL> gw{p, gc16, lane, l16, g4, n_full, tail,
+                        sh0 + SL::kOffStage + chan_lane(16 * gc16, l16, g4),
+                        sh0 + 512 * gc16 + row16_lane(l16, g4),
+                        sh0 + SL::kOffGam + 4 * (16 * gc16 + l16)};
+        gw.head_neg = -head_mult * kLog2eF;
+        gw.bias_neg = p.dt_bias ? gw.head_neg * p.dt_bias[h * D + 16 * gc16 + l16] : 0.f;
+        gw.grp_hi = g4 >= 2 ? 1.0f : 0.0f;
+        gw.grp_odd = (g4 & 1) ? 1.0f : 0.0f;
+        gw.head_y = 0.5f * head_mult;
+        gw.bias_y = p.dt_bias ? gw.head_y * p.dt_bias[h * D + 16 * gc16 + l16] : 0.f;
+        gw.gs_half = 0.5f * p.gate_scale;
+        gw.template gate_stage<SIG>(0, 0, 0);
+    };
+    lds_barrier();  // rows and beta in LDS
+    gate(2 * wave);
+    gate(2 * wave + 1);
+    lds_barrier();
+    if (wave == 0)
+        sv.a_stage(0);
+    else if (wave == 1)
+        sv.p_stage(0);
+    lds_barrier();
+    if (wave >= 2)
+        sv.solve_stage(0);
+    lds_barrier();
+    sv.wy_stage(0);  // W and U~ overwrite the staging tiles, which the gate stage has read
+    lds_barrier();
+    sw.template chunk<kChunkFull>(0, 0);
+    sw.store_state(dst, p.final_state, slab);
+}
+
 }  // namespace
 
 hipError_t launch_chunk_mfma(const FwdParams &p, hipStream_t stream)
@@ -1113,6 +1288,18 @@ hipError_t launch_chunk_mfma(const FwdParams &p, hipStream_t stream)
     FwdParams args = p;
     void *argv[] = {&args};
     return hipLaunchKernel(kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), argv, 0, stream);
+}
+
+hipError_t launch_chunk_single(const FwdParams &p, hipStream_t stream)
+{
+    const int64_t chains = p.num_seqs * p.H;
+    if (chains == 0)
+        return hipSuccess;
+    const void *kernel = p.sigmoid == kSigmoidTanh ? reinterpret_cast<const void *>(&chunk_single_kernel<kSigmoidTanh>)
+                                                   : reinterpret_cast<const void *>(&chunk_single_kernel<kSigmoidExp>);
+    FwdParams args = p;
+    void *argv[] = {&args};
+    return hipLaunchKernel(kernel, dim3(static_cast<unsigned>(chains)), dim3(256), argv, 0, stream);
 }
 
 }  // namespace kda

@@ -71,12 +71,16 @@ hipError_t launch_forward_scan(const FwdParams &p, hipStream_t stream);
 // Individual kernel launchers (one per implementation).
 hipError_t launch_chunk_mfma(const FwdParams &p, hipStream_t stream);
 hipError_t launch_chunk_simt(const FwdParams &p, hipStream_t stream);
+// The chunked stages for calls of at most one chunk (16 tokens) per sequence
+// and no cu_seqlens: one 4-wave workgroup per chain, several per compute unit.
+hipError_t launch_chunk_single(const FwdParams &p, hipStream_t stream);
 // The token recurrence for decode-shaped calls (few tokens per sequence,
 // state in and out): one small workgroup per chain.
 hipError_t launch_decode(const FwdParams &p, hipStream_t stream);
-// Calls of at most this many tokens per sequence (and no cu_seqlens) take
-// the recurrent kernel by default.
-constexpr int64_t kDecodeMaxTokens = 16;
+// Calls without cu_seqlens of at most this many tokens per sequence take the
+// recurrent kernel by default; up to one chunk (16 tokens), the single-chunk
+// kernel; longer or packed calls, the pipelined chunked kernel.
+constexpr int64_t kRecurrentMaxTokens = 8;
 // The combine step of the segmented form: for every chain and s >= 1,
 // seg_b[c][s] <- M_s seg_b[c][s-1] + seg_b[c][s] (in stored [V][K] terms).
 hipError_t launch_scan_combine(const FwdParams &p, hipStream_t stream);

@@ -177,13 +177,16 @@ const char *kda_status_string(kda_status status);
 
 /*
  * Name of the kernel kda_fwd runs for a call with T tokens per batch row
- * (varlen != 0: cu_seqlens given).  "recurrent": the token recurrence itself,
- * one small workgroup per chain, for decode-shaped calls (no cu_seqlens and
- * T <= 16), where the state traffic dominates; "mfma": the chunked kernel,
- * for everything else.  The environment variable KDA_KERNEL (mfma,
- * recurrent, or simt: a plain fp32 chunked kernel kept for cross-checks),
- * read at every call, overrides the choice.  Returns a static string; pure
- * host logic, no device work.  kda_fwd_scan always runs the chunked kernel.
+ * (varlen != 0: cu_seqlens given).  Decode-shaped calls (no cu_seqlens, at
+ * most 16 tokens), where the state traffic dominates, take "recurrent" (the
+ * token recurrence itself, T <= 8) or "single" (the chunked stages for one
+ * chunk, 8 < T <= 16), each with one small workgroup per chain; everything
+ * else takes "mfma", the pipelined chunked kernel.  The environment variable
+ * KDA_KERNEL (mfma, recurrent, single, or simt: a plain fp32 chunked kernel
+ * kept for cross-checks), read at every call, overrides the choice; single
+ * applies only to calls it can take (no cu_seqlens, T <= 16) and falls back
+ * to mfma otherwise.  Returns a static string; pure host logic, no device
+ * work.  kda_fwd_scan always runs the chunked kernel.
  */
 const char *kda_fwd_kernel(int64_t T, int varlen);
 

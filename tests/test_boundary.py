@@ -191,18 +191,23 @@ def test_auto_segment_chunks_policy():
 
 def test_kernel_choice(monkeypatch):
     """Decode-shaped calls (no cu_seqlens, at most 16 tokens) take the
-    recurrent kernel, everything else the chunked one; KDA_KERNEL overrides
-    the choice and is read at every call."""
+    recurrent kernel up to 8 tokens and the single-chunk kernel beyond,
+    everything else the pipelined chunked one; KDA_KERNEL overrides the
+    choice and is read at every call."""
     monkeypatch.delenv("KDA_KERNEL", raising=False)
     choice = kda.fwd_kernel
-    assert [choice(t) for t in (0, 1, 8, 15, 16)] == ["recurrent"] * 5
+    assert [choice(t) for t in (0, 1, 8)] == ["recurrent"] * 3
+    assert [choice(t) for t in (9, 15, 16)] == ["single"] * 3
     assert [choice(t) for t in (17, 64, 16384)] == ["mfma"] * 3
     assert choice(1, varlen=True) == choice(16, varlen=True) == "mfma"
     for forced in ("mfma", "recurrent", "simt"):
         monkeypatch.setenv("KDA_KERNEL", forced)
         assert choice(1) == choice(10000) == choice(5, varlen=True) == forced
+    monkeypatch.setenv("KDA_KERNEL", "single")
+    assert choice(0) == choice(16) == "single"
+    assert choice(17) == choice(5, varlen=True) == "mfma"
     monkeypatch.setenv("KDA_KERNEL", "no-such-kernel")
-    assert choice(1) == "recurrent" and choice(17) == "mfma"
+    assert choice(1) == "recurrent" and choice(12) == "single" and choice(17) == "mfma"
 
 
 def test_empty_token_tensors_may_be_null():

@@ -693,3 +693,104 @@ def test_beta_zero_is_pure_decay(kernel, monkeypatch):
                           device="cuda")
     x.beta.fill_(-100.0)
     check_full(f"beta zero {kernel}", x, torch.float32)
+
+
+# --------------------------------------------------------------------------
+# the single-chunk kernel (KDA_KERNEL=single): the chunked stages for calls
+# of at most 16 tokens per sequence, one 4-wave workgroup per chain
+# --------------------------------------------------------------------------
+
+@pytest.fixture
+def single_kernel(monkeypatch):
+    monkeypatch.setenv("KDA_KERNEL", "single")
+
+
+@pytest.mark.parametrize("name", ["decode_b64_t1_h32_state", "decode_b64_t8_h32_state",
+                                  "decode_b64_t15_h32_state"])
+def test_single_decode_workloads(single_kernel, name):
+    assert kda.fwd_kernel(16) == "single"
+    print(f"[case] single-chunk kernel, workload {name}", flush=True)
+    x = synth.workload(name, device="cuda")
+    check_full(f"single {name}", x, x.final_dtype)
+
+
+@pytest.mark.parametrize("T", [0, 1, 5, 15, 16])
+def test_single_lengths(single_kernel, T):
+    print(f"[case] single-chunk kernel T={T}", flush=True)
+    x = synth.make_inputs(2, T, 3, lower_bound=-5.0, seed=600 + T, init_dtype=torch.float32,
+                          device="cuda")
+    o, f = run_gpu(x, torch.float32)
+    ro, rf = oracle_of(x)
+    if T:
+        assert_close(f"single T={T} out", o, ro)
+    assert_close(f"single T={T} final", f, rf)
+
+
+@pytest.mark.parametrize("init,final", [(None, torch.bfloat16), (torch.bfloat16, torch.bfloat16),
+                                        (torch.float32, None), (None, None)])
+def test_single_state_combinations(single_kernel, init, final):
+    print(f"[case] single-chunk kernel init={init} final={final}", flush=True)
+    x = synth.make_inputs(1, 11, 3, lower_bound=-5.0, seed=610, init_dtype=init, device="cuda")
+    o, f = run_gpu(x, final)
+    ro, rf = oracle_of(x)
+    assert_close("single state combo out", o, ro)
+    if final is not None:
+        assert_close("single state combo final", f, rf)
+
+
+@pytest.mark.parametrize("case", ["lb0", "lb-0.5", "max_decay", "min_decay", "beta_zero",
+                                  "no_gate_params", "tanh"])
+def test_single_gates(single_kernel, case, monkeypatch):
+    """Gate extremes and variants on the single-chunk kernel."""
+    print(f"[case] single-chunk kernel {case}", flush=True)
+    lb = {"lb0": 0.0, "lb-0.5": -0.5}.get(case, -5.0)
+    x = synth.make_inputs(2, 16, 4, lower_bound=lb, seed=620, init_dtype=torch.float32,
+                          with_gate_params=case != "no_gate_params", device="cuda")
+    if case == "max_decay":
+        x.g.fill_(100.0)
+    if case == "min_decay":
+        x.g.fill_(-100.0)
+        x.beta.fill_(8.0)
+    if case == "beta_zero":
+        x.beta.fill_(-100.0)
+    if case == "tanh":
+        monkeypatch.setenv("KDA_SIGMOID", "tanh")
+    check_full(f"single {case}", x, torch.float32)
+
+
+def test_single_in_place_and_invariants(single_kernel):
+    x = synth.make_inputs(3, 9, 3, lower_bound=-5.0, seed=630, init_dtype=torch.float32,
+                          device="cuda")
+    o, f = run_gpu(x, torch.float32)
+    o2, f2 = run_gpu(x, torch.float32, out_fill=1.0)
+    assert np.array_equal(o, o2) and np.array_equal(f, f2)
+    x2 = synth.KdaInputs(**{**x.__dict__, "v": x.v * 2, "initial_state": x.initial_state * 2})
+    o3, f3 = run_gpu(x2, torch.float32)
+    assert np.array_equal(o3, 2 * o) and np.array_equal(f3, 2 * f)
+    st = x.initial_state.clone()
+    out = torch.empty_like(x.v)
+    kda.fwd(x.q, x.k, x.v, x.g, x.beta, x.scale, out, x.A_log, x.dt_bias, x.lower_bound,
+            initial_state=st, final_state=st)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.double().cpu().numpy(), o)
+    assert np.array_equal(st.double().cpu().numpy(), f)
+
+
+def test_single_many_chains_sampled(single_kernel):
+    print("[case] single-chunk kernel, 2048 chains", flush=True)
+    x = synth.make_inputs(2, 13, 1024, lower_bound=-5.0, seed=640, init_dtype=torch.bfloat16,
+                          device="cuda")
+    o, f = run_gpu(x, torch.bfloat16)
+    chains = [(0, 0), (0, 700), (1, 1023)]
+    for (n, h), (ro, rf) in zip(chains, oracle_of(x, chains=chains)):
+        assert_close(f"single many out[{n},:,{h}]", o[n, :, h], ro)
+        assert_close(f"single many final[{n},{h}]", f[n, h], rf)
+
+
+def test_single_falls_back_beyond_one_chunk(single_kernel):
+    """KDA_KERNEL=single applies only to calls of at most 16 tokens without
+    cu_seqlens; longer or packed calls run the chunked kernel."""
+    assert kda.fwd_kernel(17) == "mfma" and kda.fwd_kernel(8, varlen=True) == "mfma"
+    x = synth.make_inputs(1, 40, 2, lower_bound=-5.0, seed=650, init_dtype=torch.float32,
+                          device="cuda")
+    check_full("single fallback", x, torch.float32)
