@@ -1,6 +1,6 @@
-// Chunked KDA forward kernel for gfx950: bf16 MFMA for every contraction,
-// fp32 state held in accumulator registers, one workgroup of 16 waves per
-// (sequence, head) chain.
+// Chunked KDA forward kernels for gfx950: bf16 MFMA for every contraction,
+// fp32 state held in accumulator registers; the pipelined kernel runs one
+// workgroup of 16 waves per (sequence, head) chain.
 //
 // The chunk-of-16 form (gate a in log2 units, G = inclusive sum of a over
 // the chunk, Gamma = 2^G, Gamma_C = its value at the chunk's last token):
@@ -46,6 +46,10 @@
 // Iteration `it` runs the gate stage of chunk it, A and P of chunk it-1, the
 // solve of chunk it-2, WY of chunk it-3 and the state update of chunk it-4;
 // one workgroup barrier per iteration orders every hand-off through LDS.
+//
+// The same stage code also runs unpipelined, for a single chunk per chain
+// (chunk_single_kernel, at the end of this file): the stage structs take the
+// LDS layout as a template parameter.
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
