@@ -794,3 +794,19 @@ def test_single_falls_back_beyond_one_chunk(single_kernel):
     x = synth.make_inputs(1, 40, 2, lower_bound=-5.0, seed=650, init_dtype=torch.float32,
                           device="cuda")
     check_full("single fallback", x, torch.float32)
+
+
+@pytest.mark.parametrize("T,kernel", [(2, "recurrent"), (12, "single"), (17, "mfma")])
+def test_max_heads_sampled(T, kernel):
+    """H = 65536, the most heads the API takes: a grid of 65536 workgroups on
+    each of the default kernels (chosen by T); sampled heads against the
+    oracle.  No states, so the inputs stay small."""
+    assert kda.fwd_kernel(T) == kernel
+    print(f"[case] max heads T={T} ({kernel})", flush=True)
+    x = synth.make_inputs(1, T, 65536, lower_bound=-5.0, seed=700 + T, device="cuda")
+    o, _ = run_gpu(x)
+    heads = (0, 12345, 40000, 65535)
+    chains = [(0, h) for h in heads]
+    for (n, h), (ro, _) in zip(chains, oracle_of(x, chains=chains)):
+        assert_close(f"max heads T={T} out[0,:,{h}]", o[0, :, h], ro)
+    assert np.isfinite(o).all()
