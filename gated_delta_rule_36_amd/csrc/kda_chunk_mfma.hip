@@ -728,8 +728,9 @@ struct SolveWave {
 // Where a state wave's state comes from and goes to (wave-uniform).
 enum StateSrc : int { kSrcZero = 0, kSrcIdentity = 1, kSrcFp32 = 2, kSrcBf16 = 3 };
 enum ChunkMode : int { kChunkFull = 0, kChunkState = 1, kChunkTransition = 2 };
-// kDstFp32T: fp32, untransposed ([K][V]: element [k][v] = S[k][v]).
-enum StateDst : int { kDstNone = 0, kDstFp32 = 2, kDstBf16 = 3, kDstFp32T = 4 };
+// kDstHiLoT: untransposed ([K][V]: element [k][v] = S[k][v]) as two bf16
+// planes, hi = bf16(S) then lo = bf16(S - hi), in one fp32-sized slab.
+enum StateDst : int { kDstNone = 0, kDstFp32 = 2, kDstBf16 = 3, kDstHiLoT = 4 };
 
 template <class L>
 struct StateWave {
@@ -786,10 +787,16 @@ struct StateWave {
                 const int64_t idx = slab + slab_index(mt, nt);
                 if (dst == kDstFp32) {
                     *reinterpret_cast<f32x4_t *>(static_cast<float *>(ptr) + idx) = S[mt][nt];
-                } else if (dst == kDstFp32T) {
-                    float *const base = static_cast<float *>(ptr) + slab + 32 * w + 16 * nt + l16;
+                } else if (dst == kDstHiLoT) {
+                    uint16_t *const hi = static_cast<uint16_t *>(ptr) + 2 * slab + 32 * w + 16 * nt + l16;
+                    uint16_t *const lo = hi + D * D;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) base[(16 * mt + 4 * g4 + i) * D] = S[mt][nt][i];
+                    for (int i = 0; i < 4; ++i) {
+                        const float x = S[mt][nt][i];
+                        const uint16_t h = f32_to_bf16_rne(x);
+                        hi[(16 * mt + 4 * g4 + i) * D] = h;
+                        lo[(16 * mt + 4 * g4 + i) * D] = f32_to_bf16_rne(x - bf16_to_f32(h));
+                    }
                 } else {
                     *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(ptr) + idx) =
                         u32x2_t{uint32_t(f32_to_bf16_rne(S[mt][nt][0])) |
@@ -939,7 +946,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
             if (seg == 0 || seg >= segs - 1)
                 return;
             src = kSrcIdentity;
-            dst = kDstFp32T;  // M itself, [k][v]: rows of M are contiguous for the combine
+            dst = kDstHiLoT;  // M itself, [k][v], hi / lo bf16: the combine step's operands
             dst_ptr = p.seg_m;
             dst_slab = scratch;
         } else {

@@ -51,7 +51,7 @@ struct FwdParams {
     int64_t seg_chunks = 0;  // chunks per segment (phase != kPhaseWhole)
     int64_t n_seg = 1;       // segments per chain, the longest chain's count
     float *seg_b = nullptr;  // fp32 [chains][n_seg][V][K]
-    float *seg_m = nullptr;  // fp32 [chains][n_seg][K][K]: M_s itself, row-major
+    float *seg_m = nullptr;  // [chains][n_seg] fp32-sized slabs: M_s itself as bf16 hi, lo planes [K][K]
 };
 
 // Enqueue the whole forward pass on `stream`.  Returns the launch status.

@@ -133,10 +133,11 @@ kda_status kda_fwd(const void *q, const void *k, const void *v, const void *g,
  * segment but the last (segment 0 from the real initial state, the others
  * from zero), M for the inner segments (the state update with v set to zero,
  * from an identity start), a combine step that walks each chain's segments
- * in order (start of segment s+1 = M_s * start of s + b_s, in fp32), and the
- * output pass, every segment from its true start state.  M and b stay fp32,
- * so the results match kda_fwd's to within the rounding of the bf16 matrix
- * operands both forms use.
+ * in order (start of segment s+1 = M_s * start of s + b_s), and the output
+ * pass, every segment from its true start state.  b and the combined states
+ * stay fp32; M and the running state enter the combine as hi + lo bf16
+ * pairs (about 17 significant bits each), so the results match kda_fwd's to
+ * within the rounding of the bf16 matrix operands both forms use.
  *
  *   seg_chunks       chunks per segment, >= 1 (KDA_ERR_SIZE otherwise).  One
  *                    segment per chain (seg_chunks >= ceil(T / 16)) is exactly
