@@ -446,15 +446,16 @@ struct GateWave {
     // 16 channels.  FULL: all 16 rows of the chunk lie in the sequence.
     // o3, o5: offsets of chunk x's stage slot and of its Qt / Kbar ring slot
     // (x mod 3 and x mod 5 slots, kept as running offsets by the caller).
-    template <int SIG>
+    // QT: form Qt (only the output needs it; without it q is never read).
+    template <int SIG, bool QT = true>
     __device__ void gate_stage(int x, uint32_t o3, uint32_t o5) const
     {
         if (x < n_full)
-            gate_rows<true, SIG>(x, o3, o5);
+            gate_rows<true, SIG, QT>(x, o3, o5);
         else
-            gate_rows<false, SIG>(x, o3, o5);
+            gate_rows<false, SIG, QT>(x, o3, o5);
     }
-    template <bool FULL, int SIG>
+    template <bool FULL, int SIG, bool QT>
     __device__ void gate_rows(int x, uint32_t o3, uint32_t o5) const
     {
         const int len = FULL ? C : tail;
@@ -462,7 +463,7 @@ struct GateWave {
         // channel-major: the transposing read of the token-major stage tiles
         // gives lane (l16, g4) tokens 4 g4 .. 4 g4 + 3 of channel 16 gc16 + l16
         const uint32_t ar = slot_base(rd_stage + o3);
-        const f32x4_t cq = bf16x4_to_f32(lds_tr(ar));
+        const f32x4_t cq = QT ? bf16x4_to_f32(lds_tr(ar)) : f32x4_t{0.f, 0.f, 0.f, 0.f};
         const f32x4_t ck = bf16x4_to_f32(lds_tr(ar + kTile));
         const f32x4_t cg = bf16x4_to_f32(lds_tr(ar + 2 * kTile));
 
@@ -510,7 +511,8 @@ struct GateWave {
         const uint32_t a5 = slot_base(st_col + o5);  // Qt and Kbar share the ring index
         lds_st(slot_base(st_col + s4 * kTile) + kOffKt, pack_bf16x4(kt));
         lds_st(slot_base(st_col + s2 * kTile) + kOffKh, pack_bf16x4(kh));
-        lds_st(a5 + kOffQt, pack_bf16x4(qt));
+        if constexpr (QT)
+            lds_st(a5 + kOffQt, pack_bf16x4(qt));
         lds_st(a5 + kOffKb, pack_bf16x4(kb));
         if (g4 == 0)
             lds_st(st_gam + (o5 >> 3), gc);
@@ -694,7 +696,9 @@ struct SolveWave {
 
     // WY: W and U~ for channels / value columns 32 pw .. 32 pw + 31 of chunk x.
     // T diag(beta) = T_hi + T_lo (two bf16 parts) enters one 16x16x32 MFMA
-    // as the contraction [T_hi | T_lo] against [X; X].
+    // as the contraction [T_hi | T_lo] against [X; X].  UT: form U~ (the
+    // transition pass, which ignores v, does not).
+    template <bool UT = true>
     __device__ void wy_stage(int x) const
     {
         const uint32_t s2 = x & 1, s4 = x & 3, s6 = x % 6;
@@ -713,10 +717,12 @@ struct SolveWave {
             // 4 pw + g4, half t of the padded row
             const f32x4_t w = mfma32(cat8(ka, ka), t8, zero);
             lds_st(aw + 8 * t, pack_bf16x4(w));
-            const u32x2_t vb = lds_tr(av[t]);
-            // lane (vcol, g4): U~[4g4+i][vcol]
-            const f32x4_t u = mfma32(t8, cat8(vb, vb), zero);
-            lds_st(au + 64 * C * t, u);
+            if constexpr (UT) {
+                const u32x2_t vb = lds_tr(av[t]);
+                // lane (vcol, g4): U~[4g4+i][vcol]
+                const f32x4_t u = mfma32(t8, cat8(vb, vb), zero);
+                lds_st(au + 64 * C * t, u);
+            }
         }
     }
 };
@@ -903,6 +909,9 @@ template <int MODE, int INV, int SIG = kSigmoidExp>
 __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
 {
     __shared__ SharedPipe sh;
+    // Without outputs (the map passes of the segmented form) q, Qt and P are
+    // not needed; the transition pass (v ignored) needs neither v nor U~.
+    constexpr bool kOut = MODE == kChunkFull, kUt = MODE != kChunkTransition;
     // Block -> chain (and, in the segmented form, segment).  The grid is
     // below 2^31 blocks (checked on the host), so 32-bit arithmetic suffices;
     // readfirstlane keeps these wave-uniform values in scalar registers.
@@ -1036,7 +1045,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
                 if (it >= 1 && it - 1 < nc)
                     sv.a_stage(it - 1);
                 if (it >= 3 && it - 3 < nc)
-                    sv.wy_stage(it - 3);
+                    sv.template wy_stage<kUt>(it - 3);
                 lds_barrier();
                 if (it < nc)  // chunk it (even)
                     sv.put_beta(it, b_even);
@@ -1044,7 +1053,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
                 if (it < nc)
                     sv.a_stage(it);
                 if (it >= 2 && it - 2 < nc)
-                    sv.wy_stage(it - 2);
+                    sv.template wy_stage<kUt>(it - 2);
                 lds_barrier();
             }
             wait_vmem<0>();  // no load may still be writing registers when the wave ends
@@ -1054,30 +1063,34 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
             // P of chunk it - 1 and WY of chunk it - 3 each iteration; this
             // wave also loads all 16 rows of g and v two chunks ahead (g into
             // the stage ring, v into its ring for WY), like the gate waves'
-            // loads of q and k.
+            // loads of q and k.  Without outputs P is not needed, and the
+            // transition pass reads no v.
             Loader<4> lg, lv;
             lg.init(p.g + first * D, tok_bytes, 0, lane, tail, n_full, sh0 + kOffStage + 2 * kTile, 3 * kTile, 3);
             lv.init(p.v + first * D, tok_bytes, 0, lane, tail, n_full, sh0 + kOffV, kTile, 6);
             if (n_iter > 0) {
                 for (int c = 0; c < 2; ++c) {  // chunks 0 and min(1, nc - 1)
                     lg.issue();
-                    lv.issue();
+                    if constexpr (kUt)
+                        lv.issue();
                     lg.advance(nc);
                     lv.advance(nc);
                 }
-                wait_vmem<8>();  // chunk 0
+                wait_vmem<kUt ? 8 : 4>();  // chunk 0
                 lds_barrier();
             }
             for (int it = 0; it < n_iter; ++it) {
                 lg.issue();  // chunk min(it + 2, nc - 1); slots as for the gate waves' loads
-                lv.issue();
+                if constexpr (kUt)
+                    lv.issue();
                 lg.advance(nc);
                 lv.advance(nc);
-                if (it >= 1 && it - 1 < nc)
-                    sv.p_stage(it - 1);
+                if constexpr (kOut)
+                    if (it >= 1 && it - 1 < nc)
+                        sv.p_stage(it - 1);
                 if (it >= 3 && it - 3 < nc)
-                    sv.wy_stage(it - 3);
-                wait_vmem<8>();  // chunk it + 1
+                    sv.template wy_stage<kUt>(it - 3);
+                wait_vmem<kUt ? 8 : 4>();  // chunk it + 1
                 lds_barrier();
             }
             wait_vmem<0>();  // no load may still be writing LDS when the wave ends
@@ -1095,7 +1108,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
                 }
             }
             if (it >= 3 && it - 3 < nc)
-                sv.wy_stage(it - 3);
+                sv.template wy_stage<kUt>(it - 3);
             lds_barrier();
         }
         return;
@@ -1128,7 +1141,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
     // 3) sit on the critical path; the gate waves fill the issue slots they
     // leave.
     __builtin_amdgcn_s_setprio(1);
-    const bool loads = gc16 < 4;
+    const bool loads = gc16 < 4 && (kOut || gc16 >= 2);  // q only for the output
     Loader<2> ld;
     ld.init((gc16 < 2 ? p.q : p.k) + first * D, tok_bytes, 8 * (gc16 & 1), lane, tail, n_full,
             sh0 + kOffStage + (gc16 >> 1) * kTile, 3 * kTile, 3);
@@ -1148,7 +1161,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
             ld.issue();
             ld.advance(nc);
         }
-        gw.gate_stage<SIG>(it, o3, o5);
+        gw.template gate_stage<SIG, kOut>(it, o3, o5);
         o3 = o3 == 2 * (3 * kTile) ? 0 : o3 + 3 * kTile;
         o5 = o5 == 4 * kTile ? 0 : o5 + kTile;
         wait_vmem<2>();  // chunk it + 1
