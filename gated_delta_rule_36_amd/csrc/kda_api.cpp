@@ -302,19 +302,16 @@ int inverse_from_env()
     return e && std::strcmp(e, "neumann") == 0 ? kInverseNeumann : kInverseSubst;
 }
 
-// The segmented form: map (end states, then transition matrices), combine,
-// output; four launches in order on one stream.
+// The segmented form: map (end states and, with more than two segments,
+// transition matrices, in one pass), combine, output; three launches in
+// order on one stream (two when no chain has more than two segments).
 hipError_t launch_forward_scan(const FwdParams &p, hipStream_t stream)
 {
     FwdParams s = p;
-    s.phase = kPhaseMapB;
+    s.phase = p.n_seg > 2 ? kPhaseMapBM : kPhaseMapB;
     hipError_t err = launch_chunk_mfma(s, stream);
-    if (err == hipSuccess && p.n_seg > 2) {
-        s.phase = kPhaseMapM;
-        err = launch_chunk_mfma(s, stream);
-        if (err == hipSuccess)
-            err = launch_scan_combine(s, stream);
-    }
+    if (err == hipSuccess && p.n_seg > 2)
+        err = launch_scan_combine(s, stream);
     if (err == hipSuccess) {
         s.phase = kPhaseOut;
         err = launch_chunk_mfma(s, stream);

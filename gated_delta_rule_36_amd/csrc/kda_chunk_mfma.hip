@@ -386,7 +386,7 @@ struct Loader {
     uint32_t slot;                // bytes between ring slots
     int x, n_full;                // chunk being loaded; full chunks of the range
 
-    __device__ void init(const uint16_t *tensor, int64_t tok_bytes, int row0, int lane, int tail_len,
+    __device__ __forceinline__ void init(const uint16_t *tensor, int64_t tok_bytes, int row0, int lane, int tail_len,
                          int nfull, uint32_t ring0, uint32_t slot_bytes, int ring)
     {
         src = reinterpret_cast<const char *>(tensor);
@@ -405,13 +405,13 @@ struct Loader {
         n_full = nfull;
     }
     // Start loading chunk x (NJ loads; every lane loads something valid).
-    __device__ void issue() const
+    __device__ __forceinline__ void issue() const
     {
         const bool f = x < n_full;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) dma16(src, f ? full[j] : tail[j], dst + 1024 * j);
     }
-    __device__ void advance(int nc)
+    __device__ __forceinline__ void advance(int nc)
     {
         if (x < nc - 1) {
             ++x;
@@ -440,7 +440,7 @@ struct GateWave {
     // tanh form: y = x / 2 = head_y g + bias_y; a = gs_half (1 + tanh y)
     float head_y, bias_y, gs_half;
 
-    __device__ int chunk_len(int x) const { return x < n_full ? C : tail; }
+    __device__ __forceinline__ int chunk_len(int x) const { return x < n_full ? C : tail; }
 
     // Gate, decay products and decayed operands of chunk x for this wave's
     // 16 channels.  FULL: all 16 rows of the chunk lie in the sequence.
@@ -448,7 +448,7 @@ struct GateWave {
     // (x mod 3 and x mod 5 slots, kept as running offsets by the caller).
     // QT: form Qt (only the output needs it; without it q is never read).
     template <int SIG, bool QT = true>
-    __device__ void gate_stage(int x, uint32_t o3, uint32_t o5) const
+    __device__ __forceinline__ void gate_stage(int x, uint32_t o3, uint32_t o5) const
     {
         if (x < n_full)
             gate_rows<true, SIG, QT>(x, o3, o5);
@@ -456,7 +456,7 @@ struct GateWave {
             gate_rows<false, SIG, QT>(x, o3, o5);
     }
     template <bool FULL, int SIG, bool QT>
-    __device__ void gate_rows(int x, uint32_t o3, uint32_t o5) const
+    __device__ __forceinline__ void gate_rows(int x, uint32_t o3, uint32_t o5) const
     {
         const int len = FULL ? C : tail;
         const uint32_t s2 = x & 1, s4 = x & 3;
@@ -546,7 +546,7 @@ struct SolveWave {
     uint32_t bq;  // beta of tokens 4 g4 .. 4 g4 + 3 (the Neumann inverse)
 
     // The beta logits of chunk x (rows past the end read token 0).
-    __device__ uint32_t load_beta(int x) const
+    __device__ __forceinline__ uint32_t load_beta(int x) const
     {
         uint32_t off = beta_lane;
         if (x >= n_full)
@@ -554,7 +554,7 @@ struct SolveWave {
         return gload_u16(base_beta + int64_t(x) * beta_chunk_bytes + off);
     }
     // sigmoid(beta) of chunk x into its ring slot, 0 on rows past the end.
-    __device__ void put_beta(int x, uint32_t logit) const
+    __device__ __forceinline__ void put_beta(int x, uint32_t logit) const
     {
         const int len = x < n_full ? C : tail;
         const float b = sigmoid_f32(bf16_to_f32(static_cast<uint16_t>(logit)));
@@ -563,7 +563,7 @@ struct SolveWave {
     }
 
     // -A of chunk x: lane (j = l16, g4) gets (Kt Kh^T)[4 g4 + e][j].
-    __device__ void a_stage(int x) const
+    __device__ __forceinline__ void a_stage(int x) const
     {
         const uint32_t s2 = x & 1, s3 = x % 3, s4 = x & 3;
         const uint32_t ak = slot_base(tok + s4 * kTile + kOffKt), ah = slot_base(tok + s2 * kTile + kOffKh);
@@ -582,7 +582,7 @@ struct SolveWave {
 
     // P of chunk x, as P^T = Kh Qt^T: lane (i = l16, g4) gets
     // P[i][4 g4 .. 4 g4 + 3], the layout the state stage reads.
-    __device__ void p_stage(int x) const
+    __device__ __forceinline__ void p_stage(int x) const
     {
         const uint32_t s2 = x & 1, s4 = x & 3, s5 = x % 5;
         const uint32_t ah = slot_base(tok + s2 * kTile + kOffKh), aq = slot_base(tok + s5 * kTile + kOffQt);
@@ -598,7 +598,7 @@ struct SolveWave {
 
     // Columns 8 (pw - 2) .. 8 (pw - 2) + 7 of T for chunk x (solve waves 2
     // and 3), stored as T diag(beta).
-    __device__ void solve_stage(int x) const
+    __device__ __forceinline__ void solve_stage(int x) const
     {
         const uint32_t s2 = x & 1, s3 = x % 3;
         // T[:, j] for j = j0, j0 + 1 with j0 = 8 (pw - 2) + 2 g4; lane
@@ -641,7 +641,7 @@ struct SolveWave {
     // operand of X^T as it stands, so each power is also formed transposed
     // and no value moves between lanes; the last product gives T^T, i.e. row
     // l16 of T in lane (l16, g4), the layout T diag(beta) is stored in.
-    __device__ void solve_neumann(int x) const
+    __device__ __forceinline__ void solve_neumann(int x) const
     {
         const uint32_t s2 = x & 1, s3 = x % 3;
         f32x4_t eye;  // the identity in either layout: (l16 == 4 g4 + r)
@@ -699,7 +699,7 @@ struct SolveWave {
     // as the contraction [T_hi | T_lo] against [X; X].  UT: form U~ (the
     // transition pass, which ignores v, does not).
     template <bool UT = true>
-    __device__ void wy_stage(int x) const
+    __device__ __forceinline__ void wy_stage(int x) const
     {
         const uint32_t s2 = x & 1, s4 = x & 3, s6 = x % 6;
         const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
@@ -734,6 +734,9 @@ struct SolveWave {
 // Where a state wave's state comes from and goes to (wave-uniform).
 enum StateSrc : int { kSrcZero = 0, kSrcIdentity = 1, kSrcFp32 = 2, kSrcBf16 = 3 };
 enum ChunkMode : int { kChunkFull = 0, kChunkState = 1, kChunkTransition = 2 };
+// Kernel mode of the fused map pass: waves 0-3 carry the end state
+// (kChunkState), waves 4-7 the transition matrix (kChunkTransition).
+constexpr int kChunkMapBM = 3;
 // kDstHiLoT: untransposed ([K][V]: element [k][v] = S[k][v]) as two bf16
 // planes, hi = bf16(S) then lo = bf16(S - hi), in one fp32-sized slab.
 enum StateDst : int { kDstNone = 0, kDstFp32 = 2, kDstBf16 = 3, kDstHiLoT = 4 };
@@ -754,13 +757,13 @@ struct StateWave {
     f32x4_t S[8][2];     // S[16mt + 4g4 + i][32w + 16nt + l16]
 
     // Element offset, within one [V][K] state slab, of this lane's tile (mt, nt).
-    __device__ int64_t slab_index(int mt, int nt) const
+    __device__ __forceinline__ int64_t slab_index(int mt, int nt) const
     {
         return int64_t(32 * w + 16 * nt + l16) * D + 16 * mt + 4 * g4;
     }
 
     // slab: element offset of the [V][K] slab in ptr.
-    __device__ void load_state(int src, const void *ptr, int64_t slab)
+    __device__ __forceinline__ void load_state(int src, const void *ptr, int64_t slab)
     {
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
@@ -782,7 +785,7 @@ struct StateWave {
             }
     }
 
-    __device__ void store_state(int dst, void *ptr, int64_t slab) const
+    __device__ __forceinline__ void store_state(int dst, void *ptr, int64_t slab) const
     {
         if (dst == kDstNone)
             return;
@@ -817,7 +820,7 @@ struct StateWave {
     // Y, no output); kChunkTransition: the state with v ignored (U = -W S),
     // which carries an identity start to the range's transition matrix.
     template <int MODE>
-    __device__ void chunk(int x, uint32_t o5)
+    __device__ __forceinline__ void chunk(int x, uint32_t o5)
     {
         constexpr bool kOut = MODE == kChunkFull;
         const uint32_t s2 = x & 1, s4 = x & 3;
@@ -901,17 +904,22 @@ __device__ __forceinline__ void state_loop(StateWave<L> &sw, int n_iter, int nc)
 }
 
 // MODE: the state waves' chunk mode (kChunkFull for whole chains and the
-// output pass, kChunkState for the segment end states, kChunkTransition for
-// the segment transition matrices).  One mode per kernel: with several state
-// loops in one kernel the compiler runs out of registers.
+// output pass, kChunkState for the segment end states), or kChunkMapBM for
+// the fused map pass of the segmented form: eight state waves, 0-3 for the
+// segment's end state from its start (kChunkState) and 4-7 for its
+// transition matrix from the identity (kChunkTransition), and four gate
+// waves of 32 channels each (8-11); the gate and solve work and the loads
+// are shared by both states.
 // INV: the inverse (Inverse); SIG: the gate's logistic function (Sigmoid).
 template <int MODE, int INV, int SIG = kSigmoidExp>
 __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
 {
     __shared__ SharedPipe sh;
     // Without outputs (the map passes of the segmented form) q, Qt and P are
-    // not needed; the transition pass (v ignored) needs neither v nor U~.
+    // not needed; a transition-only pass (v ignored) needs neither v nor U~.
+    constexpr bool kFused = MODE == kChunkMapBM;
     constexpr bool kOut = MODE == kChunkFull, kUt = MODE != kChunkTransition;
+    constexpr int kStateWaves = kFused ? 8 : 4;
     // Block -> chain (and, in the segmented form, segment).  The grid is
     // below 2^31 blocks (checked on the host), so 32-bit arithmetic suffices;
     // readfirstlane keeps these wave-uniform values in scalar registers.
@@ -940,23 +948,16 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
         const int64_t nc_chain = (t_end - t_begin + C - 1) / C;
         const int segs = static_cast<int>(nc_chain > 0 ? (nc_chain + p.seg_chunks - 1) / p.seg_chunks : 1);
         const int64_t scratch = (int64_t(chain) * n_seg + seg) * D * D;
-        if (p.phase == kPhaseMapB) {
+        if (p.phase == kPhaseMapB || p.phase == kPhaseMapBM) {
             // b_s for segments 0 .. segs - 2: segment 0 from the real start,
-            // later ones from zero
+            // later ones from zero (and, fused, M_s for 1 .. segs - 2 into
+            // seg_m at the same slab index)
             if (seg >= segs - 1)
                 return;
             if (seg > 0)
                 src = kSrcZero;
             dst = kDstFp32;
             dst_ptr = p.seg_b;
-            dst_slab = scratch;
-        } else if (p.phase == kPhaseMapM) {
-            // M_s for segments 1 .. segs - 2 (segment 0 starts from a known state)
-            if (seg == 0 || seg >= segs - 1)
-                return;
-            src = kSrcIdentity;
-            dst = kDstHiLoT;  // M itself, [k][v], hi / lo bf16: the combine step's operands
-            dst_ptr = p.seg_m;
             dst_slab = scratch;
         } else {
             // outputs of every segment from its true start state: the real
@@ -987,23 +988,36 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
     const int64_t first = (row * p.T + t_begin) * p.H + h;  // token-head row of t_begin
     const uint32_t sh0 = lds_addr(&sh);
 
-    if (wave < 4) {
-        StateWave<PipeLayout> sw{p, wave, lane, l16, g4, n_full, tail,
-                                  reinterpret_cast<char *>(p.out + first * D + 32 * wave),
+    if (wave < kStateWaves) {
+        const int w = wave & 3;  // value columns 32 w .. 32 w + 31
+        StateWave<PipeLayout> sw{p, w, lane, l16, g4, n_full, tail,
+                                  reinterpret_cast<char *>(p.out + first * D + 32 * w),
                                   C * tok_bytes,
                                   static_cast<uint32_t>(l16 * tok_bytes + 16 * g4),
                                   sh0 + kOffQt + tok_lane(l16, g4),
                                   sh0 + kOffW + 2 * kWPitch * l16 + 16 * g4,
-                                  sh0 + kOffU + 128 * C * wave + row32_lane(l16, g4),
+                                  sh0 + kOffU + 128 * C * w + row32_lane(l16, g4),
                                   sh0 + kOffP + row16_lane(l16, g4),
                                   sh0 + kOffGam + 16 * g4,
                                   sh0 + kOffKb + row16_lane(l16, g4),
                                   {}};
         __builtin_amdgcn_s_setprio(3);
+        if constexpr (kFused) {
+            if (wave >= 4) {
+                // M_s: from the identity, v ignored; segment 0 starts from a
+                // known state, so its matrix is not stored
+                sw.load_state(kSrcIdentity, nullptr, 0);
+                if (n_iter > 0)
+                    lds_barrier();  // the gate waves' first loads are in LDS
+                state_loop<kChunkTransition, PipeLayout>(sw, n_iter, nc);
+                sw.store_state(seg > 0 ? kDstHiLoT : kDstNone, p.seg_m, dst_slab);
+                return;
+            }
+        }
         sw.load_state(src, src_ptr, src_slab);
         if (n_iter > 0)
             lds_barrier();  // the gate waves' first loads are in LDS
-        state_loop<MODE, PipeLayout>(sw, n_iter, nc);
+        state_loop<kFused ? kChunkState : MODE, PipeLayout>(sw, n_iter, nc);
         sw.store_state(dst, dst_ptr, dst_slab);
         return;
     }
@@ -1114,20 +1128,25 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
         return;
     }
 
-    // gate waves
-    const int gc16 = wave - 4;
-    GateWave<PipeLayout> gw{p, gc16, lane, l16, g4, n_full, tail,
-                sh0 + kOffStage + chan_lane(16 * gc16, l16, g4),
-                sh0 + 512 * gc16 + row16_lane(l16, g4),
-                sh0 + kOffGam + 4 * (16 * gc16 + l16)};
+    // gate waves: channels 16 gc16 .. 16 gc16 + 15 (and, fused, 16 gc16 + 64 ..)
+    const int gc16 = wave - kStateWaves;
     const float head_mult = p.A_log ? expf(p.A_log[h]) : 1.0f;
-    gw.head_neg = -head_mult * kLog2eF;
-    gw.bias_neg = p.dt_bias ? gw.head_neg * p.dt_bias[h * D + 16 * gc16 + l16] : 0.f;
-    gw.head_y = 0.5f * head_mult;  // x / 2 = exp(A_log) (g + dt_bias) / 2
-    gw.bias_y = p.dt_bias ? gw.head_y * p.dt_bias[h * D + 16 * gc16 + l16] : 0.f;
-    gw.gs_half = 0.5f * p.gate_scale;
-    gw.grp_hi = g4 >= 2 ? 1.0f : 0.0f;
-    gw.grp_odd = (g4 & 1) ? 1.0f : 0.0f;
+    auto gate_wave = [&](int gc) {
+        GateWave<PipeLayout> g{p, gc, lane, l16, g4, n_full, tail,
+                               sh0 + kOffStage + chan_lane(16 * gc, l16, g4),
+                               sh0 + 512 * gc + row16_lane(l16, g4),
+                               sh0 + kOffGam + 4 * (16 * gc + l16)};
+        g.head_neg = -head_mult * kLog2eF;
+        g.bias_neg = p.dt_bias ? g.head_neg * p.dt_bias[h * D + 16 * gc + l16] : 0.f;
+        g.head_y = 0.5f * head_mult;  // x / 2 = exp(A_log) (g + dt_bias) / 2
+        g.bias_y = p.dt_bias ? g.head_y * p.dt_bias[h * D + 16 * gc + l16] : 0.f;
+        g.gs_half = 0.5f * p.gate_scale;
+        g.grp_hi = g4 >= 2 ? 1.0f : 0.0f;
+        g.grp_odd = (g4 & 1) ? 1.0f : 0.0f;
+        return g;
+    };
+    const GateWave<PipeLayout> gw = gate_wave(gc16);
+    const GateWave<PipeLayout> gw2 = gate_wave(kFused ? gc16 + 4 : gc16);
     if (n_iter == 0)
         return;
 
@@ -1140,11 +1159,13 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
     // (6, 7); waves 8-11 load nothing.  The state and solve waves (priority
     // 3) sit on the critical path; the gate waves fill the issue slots they
     // leave.
+    // Fused, waves 8-9 load the rows of k (q is not needed).
     __builtin_amdgcn_s_setprio(1);
-    const bool loads = gc16 < 4 && (kOut || gc16 >= 2);  // q only for the output
+    const int tensor = kFused ? 1 : gc16 >> 1;  // 0: q, 1: k
+    const bool loads = kFused ? gc16 < 2 : gc16 < 4 && (kOut || gc16 >= 2);  // q only for the output
     Loader<2> ld;
-    ld.init((gc16 < 2 ? p.q : p.k) + first * D, tok_bytes, 8 * (gc16 & 1), lane, tail, n_full,
-            sh0 + kOffStage + (gc16 >> 1) * kTile, 3 * kTile, 3);
+    ld.init((tensor == 0 ? p.q : p.k) + first * D, tok_bytes, 8 * (gc16 & 1), lane, tail, n_full,
+            sh0 + kOffStage + tensor * kTile, 3 * kTile, 3);
     if (loads) {
         for (int c = 0; c < 2; ++c) {  // chunks 0 and min(1, nc - 1)
             ld.issue();
@@ -1162,6 +1183,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
             ld.advance(nc);
         }
         gw.template gate_stage<SIG, kOut>(it, o3, o5);
+        if constexpr (kFused)
+            gw2.template gate_stage<SIG, false>(it, o3, o5);
         o3 = o3 == 2 * (3 * kTile) ? 0 : o3 + 3 * kTile;
         o5 = o5 == 4 * kTile ? 0 : o5 + kTile;
         wait_vmem<2>();  // chunk it + 1
@@ -1299,13 +1322,13 @@ hipError_t launch_chunk_mfma(const FwdParams &p, hipStream_t stream)
     const int64_t blocks = p.phase == kPhaseWhole ? chains : chains * p.n_seg;
     const void *kernel;
     if (p.inverse == kInverseNeumann)
-        kernel = p.phase == kPhaseMapB   ? reinterpret_cast<const void *>(&chunk_mfma_kernel<kChunkState, kInverseNeumann>)
-                 : p.phase == kPhaseMapM ? reinterpret_cast<const void *>(&chunk_mfma_kernel<kChunkTransition, kInverseNeumann>)
-                                         : reinterpret_cast<const void *>(&chunk_mfma_kernel<kChunkFull, kInverseNeumann>);
+        kernel = p.phase == kPhaseMapB    ? reinterpret_cast<const void *>(&chunk_mfma_kernel<kChunkState, kInverseNeumann>)
+                 : p.phase == kPhaseMapBM ? reinterpret_cast<const void *>(&chunk_mfma_kernel<kChunkMapBM, kInverseNeumann>)
+                                          : reinterpret_cast<const void *>(&chunk_mfma_kernel<kChunkFull, kInverseNeumann>);
     else
-        kernel = p.phase == kPhaseMapB   ? reinterpret_cast<const void *>(&chunk_mfma_kernel<kChunkState, kInverseSubst>)
-                 : p.phase == kPhaseMapM ? reinterpret_cast<const void *>(&chunk_mfma_kernel<kChunkTransition, kInverseSubst>)
-                                         : reinterpret_cast<const void *>(&chunk_mfma_kernel<kChunkFull, kInverseSubst>);
+        kernel = p.phase == kPhaseMapB    ? reinterpret_cast<const void *>(&chunk_mfma_kernel<kChunkState, kInverseSubst>)
+                 : p.phase == kPhaseMapBM ? reinterpret_cast<const void *>(&chunk_mfma_kernel<kChunkMapBM, kInverseSubst>)
+                                          : reinterpret_cast<const void *>(&chunk_mfma_kernel<kChunkFull, kInverseSubst>);
     // the tanh-form gate is built for whole chains with the default inverse
     if (p.sigmoid == kSigmoidTanh && p.phase == kPhaseWhole && p.inverse == kInverseSubst)
         kernel = reinterpret_cast<const void *>(&chunk_mfma_kernel<kChunkFull, kInverseSubst, kSigmoidTanh>);

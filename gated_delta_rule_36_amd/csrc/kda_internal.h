@@ -11,7 +11,7 @@ constexpr int kChunk = 16;     // tokens per chunk (fixed, as on the chunk-size 
 constexpr int kHeadDim = 128;  // K = V = 128
 
 enum StateKind : int { kStateNone = 0, kStateBf16 = 1, kStateFp32 = 2 };
-enum Phase : int { kPhaseWhole = 0, kPhaseMapB = 1, kPhaseMapM = 2, kPhaseOut = 3 };
+enum Phase : int { kPhaseWhole = 0, kPhaseMapB = 1, kPhaseMapBM = 2, kPhaseOut = 3 };
 // How the MFMA kernel forms T = (I + A)^-1: fp32 forward substitution (the
 // default) or the fp16 Neumann product (KDA_INVERSE=neumann; an ablation).
 enum Inverse : int { kInverseSubst = 0, kInverseNeumann = 1 };
@@ -43,10 +43,11 @@ struct FwdParams {
     // (the recurrence is affine in the state).  Phases: kPhaseWhole (whole
     // chains, kda_fwd); kPhaseMapB: b_s of segments 0 .. last-1 into seg_b
     // (segment 0 from the real initial state, the others from zero);
-    // kPhaseMapM: M_s of segments 1 .. last-1 into seg_m (identity start, v
-    // ignored); then the combine step turns seg_b[s] into the true start
-    // state of segment s + 1; kPhaseOut: every segment from its true start
-    // state, writing outputs, and the final state from the last segment.
+    // kPhaseMapBM: the same and, in the same pass, M_s of segments
+    // 1 .. last-1 into seg_m (identity start, v ignored); then the combine
+    // step turns seg_b[s] into the true start state of segment s + 1;
+    // kPhaseOut: every segment from its true start state, writing outputs,
+    // and the final state from the last segment.
     int phase = 0;
     int64_t seg_chunks = 0;  // chunks per segment (phase != kPhaseWhole)
     int64_t n_seg = 1;       // segments per chain, the longest chain's count
