@@ -358,6 +358,15 @@ def test_scan_ragged_lengths(T, seg):
     check_full(f"scan T={T} seg={seg}", x, torch.float32, segment_chunks=seg)
 
 
+def test_scan_chain_count_not_multiple_of_8():
+    """10 chains of 10 segments: the combine places the 8 blocks of chains
+    0-7 on one XCD each and maps chains 8-9 plainly, in one grid."""
+    print("[case] scan 10 chains x 10 segments", flush=True)
+    x = synth.make_inputs(2, 300, 5, lower_bound=-5.0, seed=36, init_dtype=torch.float32,
+                          device="cuda")
+    check_full("scan 10 chains", x, torch.float32, segment_chunks=2)
+
+
 @pytest.mark.parametrize("state,seg", [(torch.bfloat16, 1), (torch.float32, 2), (torch.bfloat16, 3)])
 def test_scan_varlen_edges(state, seg):
     lens = [1, 16, 17, 0, 33, 5, 48, 2, 130]
