@@ -129,15 +129,17 @@ kda_status kda_fwd(const void *q, const void *k, const void *v, const void *g,
  *
  * Each chain is cut into segments of seg_chunks chunks (16 tokens each).
  * The recurrence above is affine in the state, so a segment maps its start
- * state S to M S + b.  The call enqueues four steps on `stream`: b for every
- * segment but the last (segment 0 from the real initial state, the others
- * from zero), M for the inner segments (the state update with v set to zero,
- * from an identity start), a combine step that walks each chain's segments
- * in order (start of segment s+1 = M_s * start of s + b_s), and the output
- * pass, every segment from its true start state.  b and the combined states
- * stay fp32; M and the running state enter the combine as hi + lo bf16
- * pairs (about 17 significant bits each), so the results match kda_fwd's to
- * within the rounding of the bf16 matrix operands both forms use.
+ * state S to M S + b.  The call enqueues three steps on `stream`: one pass
+ * that computes b for every segment but the last (segment 0 from the real
+ * initial state, the others from zero) and M for the inner segments (the
+ * state update with v set to zero, from an identity start), a combine step
+ * that walks each chain's segments in order (start of segment s+1 =
+ * M_s * start of s + b_s), and the output pass, every segment from its true
+ * start state (two steps when no chain has more than two segments).  b and
+ * the combined states stay fp32; M and the running state enter the combine
+ * as hi + lo bf16 pairs (about 17 significant bits each), so the results
+ * match kda_fwd's to within the rounding of the bf16 matrix operands both
+ * forms use.
  *
  *   seg_chunks       chunks per segment, >= 1 (KDA_ERR_SIZE otherwise).  One
  *                    segment per chain (seg_chunks >= ceil(T / 16)) is exactly
