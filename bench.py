@@ -3,7 +3,7 @@
 One step = one forward call over the whole workload (every stage of the
 forward pass runs inside it), inputs already resident in HBM: ``kda_fwd``,
 or for workloads with few chains the segmented form ``kda_fwd_scan``
-(``--segment-chunks``; its four launches together make the step).
+(``--segment-chunks``; its three launches together make the step).
 ``kda_fwd`` runs the chunked kernel, or for decode-shaped workloads (at most
 16 tokens per sequence) the recurrent one; ``config.kernel`` names it.  The default
 workload is the large throughput case: B=8, T=16384, H=32, K=V=128,

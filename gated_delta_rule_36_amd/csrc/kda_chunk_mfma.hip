@@ -696,9 +696,7 @@ struct SolveWave {
 
     // WY: W and U~ for channels / value columns 32 pw .. 32 pw + 31 of chunk x.
     // T diag(beta) = T_hi + T_lo (two bf16 parts) enters one 16x16x32 MFMA
-    // as the contraction [T_hi | T_lo] against [X; X].  UT: form U~ (the
-    // transition pass, which ignores v, does not).
-    template <bool UT = true>
+    // as the contraction [T_hi | T_lo] against [X; X].
     __device__ __forceinline__ void wy_stage(int x) const
     {
         const uint32_t s2 = x & 1, s4 = x & 3, s6 = x % 6;
@@ -717,12 +715,10 @@ struct SolveWave {
             // 4 pw + g4, half t of the padded row
             const f32x4_t w = mfma32(cat8(ka, ka), t8, zero);
             lds_st(aw + 8 * t, pack_bf16x4(w));
-            if constexpr (UT) {
-                const u32x2_t vb = lds_tr(av[t]);
-                // lane (vcol, g4): U~[4g4+i][vcol]
-                const f32x4_t u = mfma32(t8, cat8(vb, vb), zero);
-                lds_st(au + 64 * C * t, u);
-            }
+            const u32x2_t vb = lds_tr(av[t]);
+            // lane (vcol, g4): U~[4g4+i][vcol]
+            const f32x4_t u = mfma32(t8, cat8(vb, vb), zero);
+            lds_st(au + 64 * C * t, u);
         }
     }
 };
@@ -916,9 +912,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
 {
     __shared__ SharedPipe sh;
     // Without outputs (the map passes of the segmented form) q, Qt and P are
-    // not needed; a transition-only pass (v ignored) needs neither v nor U~.
+    // not needed.
     constexpr bool kFused = MODE == kChunkMapBM;
-    constexpr bool kOut = MODE == kChunkFull, kUt = MODE != kChunkTransition;
+    constexpr bool kOut = MODE == kChunkFull;
     constexpr int kStateWaves = kFused ? 8 : 4;
     // Block -> chain (and, in the segmented form, segment).  The grid is
     // below 2^31 blocks (checked on the host), so 32-bit arithmetic suffices;
@@ -1059,7 +1055,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
                 if (it >= 1 && it - 1 < nc)
                     sv.a_stage(it - 1);
                 if (it >= 3 && it - 3 < nc)
-                    sv.template wy_stage<kUt>(it - 3);
+                    sv.wy_stage(it - 3);
                 lds_barrier();
                 if (it < nc)  // chunk it (even)
                     sv.put_beta(it, b_even);
@@ -1067,7 +1063,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
                 if (it < nc)
                     sv.a_stage(it);
                 if (it >= 2 && it - 2 < nc)
-                    sv.template wy_stage<kUt>(it - 2);
+                    sv.wy_stage(it - 2);
                 lds_barrier();
             }
             wait_vmem<0>();  // no load may still be writing registers when the wave ends
@@ -1077,34 +1073,31 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
             // P of chunk it - 1 and WY of chunk it - 3 each iteration; this
             // wave also loads all 16 rows of g and v two chunks ahead (g into
             // the stage ring, v into its ring for WY), like the gate waves'
-            // loads of q and k.  Without outputs P is not needed, and the
-            // transition pass reads no v.
+            // loads of q and k.  Without outputs P is not needed.
             Loader<4> lg, lv;
             lg.init(p.g + first * D, tok_bytes, 0, lane, tail, n_full, sh0 + kOffStage + 2 * kTile, 3 * kTile, 3);
             lv.init(p.v + first * D, tok_bytes, 0, lane, tail, n_full, sh0 + kOffV, kTile, 6);
             if (n_iter > 0) {
                 for (int c = 0; c < 2; ++c) {  // chunks 0 and min(1, nc - 1)
                     lg.issue();
-                    if constexpr (kUt)
-                        lv.issue();
+                    lv.issue();
                     lg.advance(nc);
                     lv.advance(nc);
                 }
-                wait_vmem<kUt ? 8 : 4>();  // chunk 0
+                wait_vmem<8>();  // chunk 0
                 lds_barrier();
             }
             for (int it = 0; it < n_iter; ++it) {
                 lg.issue();  // chunk min(it + 2, nc - 1); slots as for the gate waves' loads
-                if constexpr (kUt)
-                    lv.issue();
+                lv.issue();
                 lg.advance(nc);
                 lv.advance(nc);
                 if constexpr (kOut)
                     if (it >= 1 && it - 1 < nc)
                         sv.p_stage(it - 1);
                 if (it >= 3 && it - 3 < nc)
-                    sv.template wy_stage<kUt>(it - 3);
-                wait_vmem<kUt ? 8 : 4>();  // chunk it + 1
+                    sv.wy_stage(it - 3);
+                wait_vmem<8>();  // chunk it + 1
                 lds_barrier();
             }
             wait_vmem<0>();  // no load may still be writing LDS when the wave ends
@@ -1122,7 +1115,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
                 }
             }
             if (it >= 3 && it - 3 < nc)
-                sv.template wy_stage<kUt>(it - 3);
+                sv.wy_stage(it - 3);
             lds_barrier();
         }
         return;
