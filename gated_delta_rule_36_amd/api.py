@@ -169,7 +169,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
 def fwd_kernel(T: int, varlen: bool = False) -> str:
     """Name of the kernel ``fwd`` runs for a call with ``T`` tokens per batch
     row (``varlen``: cu_seqlens given), as the library decides it (including
-    the KDA_KERNEL override): "recurrent", "mfma" or "simt".  The segmented
+    the KDA_KERNEL override): "recurrent", "single", "mfma" or "simt".  The segmented
     form (``segment_chunks``) always runs the chunked kernel."""
     return _lib.load().kda_fwd_kernel(int(T), 1 if varlen else 0).decode()
 

@@ -819,3 +819,50 @@ def test_max_heads_sampled(T, kernel):
     for (n, h), (ro, _) in zip(chains, oracle_of(x, chains=chains)):
         assert_close(f"max heads T={T} out[0,:,{h}]", o[0, :, h], ro)
     assert np.isfinite(o).all()
+
+
+# --------------------------------------------------------------------------
+# HIP graph capture (serving loops replay a captured call)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,seg,kernel", [(3, None, "recurrent"), (12, None, "single"),
+                                          (100, None, "mfma"), (600, 2, "segmented")])
+def test_graph_capture_replays(T, seg, kernel):
+    """kda.fwd captured in a HIP graph (torch.cuda.CUDAGraph) and replayed
+    three times, with new inputs copied in and the outputs cleared (eager
+    work) and a synchronisation between replays: every replay equals the
+    eager call on the same inputs bit for bit, and the last one the oracle."""
+    B, H = (4, 4) if seg is None else (1, 2)
+    if seg is None:
+        assert kda.fwd_kernel(T) == kernel
+    print(f"[case] graph capture {kernel} B={B} T={T} H={H}", flush=True)
+    x = synth.make_inputs(B, T, H, lower_bound=-5.0, seed=900 + T, init_dtype=torch.float32,
+                          device="cuda")
+    out, fin = torch.empty_like(x.v), torch.empty_like(x.initial_state)
+    ref_out, ref_fin = torch.empty_like(out), torch.empty_like(fin)
+
+    def call(o, f):
+        kda.fwd(x.q, x.k, x.v, x.g, x.beta, x.scale, o, x.A_log, x.dt_bias, x.lower_bound,
+                initial_state=x.initial_state, final_state=f, segment_chunks=seg)
+
+    call(out, fin)  # outside the capture first (loads the library)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(out, fin)
+    for r in range(3):
+        y = synth.make_inputs(B, T, H, lower_bound=-5.0, seed=910 + 10 * T + r,
+                              init_dtype=torch.float32, device="cuda")
+        for name in ("q", "k", "v", "g", "beta", "initial_state"):
+            getattr(x, name).copy_(getattr(y, name))
+        out.zero_()
+        fin.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        call(ref_out, ref_fin)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(fin, ref_fin), f"replay {r} differs from the eager call"
+    ro, rf = oracle_of(x)
+    assert_close(f"graph {kernel} out", out.double().cpu().numpy(), ro)
+    assert_close(f"graph {kernel} final", fin.double().cpu().numpy(), rf)
