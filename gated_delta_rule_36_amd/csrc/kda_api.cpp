@@ -205,8 +205,10 @@ extern "C" kda_status kda_fwd_scan(const void *q, const void *k, const void *v, 
         return st;
     const int64_t n_seg = segments_per_chain(T, seg_chunks);
     int64_t blocks;
-    // grids: chains * n_seg blocks for the map and output passes
-    if (n_seg < 0 || !mul_ok(c.chains, n_seg, &blocks) || blocks > INT32_MAX)
+    // grids: chains * n_seg blocks for the map and output passes, chains * 8
+    // for the combine step (run with more than two segments)
+    if (n_seg < 0 || !mul_ok(c.chains, n_seg, &blocks) || blocks > INT32_MAX ||
+        (n_seg > 2 && c.chains > INT32_MAX / 8))
         return KDA_ERR_SIZE;
     const int64_t need = blocks * 2 * kSlabBytes;
     if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 16 != 0)

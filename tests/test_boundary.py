@@ -179,6 +179,18 @@ def test_scan_argument_errors_are_reported_before_launch(kw, code):
     assert call_scan(**args, **over) == code
 
 
+def test_scan_combine_grid_limit():
+    """With more than two segments the combine step runs 8 blocks per chain:
+    more than INT32_MAX / 8 chains is a size error, reported before the
+    workspace is looked at, even where chains x segments still fits."""
+    tb = 1 << 44  # fake addresses 16 TiB apart, never dereferenced: no declared spans overlap
+    fake = {n: (i + 1) * tb for i, n in enumerate(["q", "k", "v", "g", "beta", "out", "A_log", "dt_bias"])}
+    B, H = 4097, 65536  # 268,500,992 chains: above 2^31 / 8, and x 3 segments below 2^31
+    assert call_scan(seg=1, ws=None, T=48, B=B, H=H, **fake) == _lib.KDA_ERR_SIZE
+    # one segment per chain: no combine step, so the missing workspace is the error
+    assert call_scan(seg=16, ws=None, T=48, B=B, H=H, **fake) == _lib.KDA_ERR_WORKSPACE
+
+
 def test_auto_segment_chunks_policy():
     auto = kda.auto_segment_chunks
     assert auto(16, 8192) == 32          # 16 chains x 16 segments of 32 chunks
