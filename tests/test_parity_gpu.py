@@ -358,6 +358,20 @@ def test_scan_ragged_lengths(T, seg):
     check_full(f"scan T={T} seg={seg}", x, torch.float32, segment_chunks=seg)
 
 
+def test_scan_many_segments():
+    """One chain of 8192 tokens in segments of 2 chunks: 256 segments, so the
+    combine step chains 254 products on hi/lo bf16 operands; its rounding
+    must not build up (final state against the oracle and the whole-chain
+    kernel)."""
+    print("[case] scan 1 chain x 256 segments", flush=True)
+    x = synth.make_inputs(1, 8192, 1, lower_bound=-3.0, seed=37, init_dtype=torch.float32,
+                          device="cuda")
+    o, f = check_full("scan 256 segments", x, torch.float32, segment_chunks=2)
+    o1, f1 = run_gpu(x, torch.float32)
+    assert_close("scan 256 segments vs whole out", o, o1)
+    assert_close("scan 256 segments vs whole final", f, f1)
+
+
 def test_scan_chain_count_not_multiple_of_8():
     """10 chains of 10 segments: the combine places the 8 blocks of chains
     0-7 on one XCD each and maps chains 8-9 plainly, in one grid."""
