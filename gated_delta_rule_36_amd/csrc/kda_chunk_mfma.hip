@@ -922,8 +922,18 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
     const int n_seg = static_cast<int>(p.n_seg);
     int chain = blockIdx.x, seg = 0;
     if (p.phase != kPhaseWhole) {
-        chain = static_cast<int>(blockIdx.x) / n_seg;
-        seg = static_cast<int>(blockIdx.x) - chain * n_seg;
+        // chain c's segments on XCD c mod 8 (blocks go to XCD b mod 8), where
+        // the combine step reads them
+        const int b = static_cast<int>(blockIdx.x);
+        const int whole = static_cast<int>(p.num_seqs * p.H / 8) * 8 * n_seg;
+        if (b < whole) {
+            const int i = b >> 3;
+            chain = 8 * (i / n_seg) + (b & 7);
+            seg = i % n_seg;
+        } else {
+            chain = b / n_seg;
+            seg = b - chain * n_seg;
+        }
     }
     chain = __builtin_amdgcn_readfirstlane(chain);
     seg = __builtin_amdgcn_readfirstlane(seg);
