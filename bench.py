@@ -4,11 +4,17 @@ One step = one forward call over the whole workload (every stage of the
 forward pass runs inside it), inputs already resident in HBM: ``kda_fwd``,
 or for workloads with few chains the segmented form ``kda_fwd_scan``
 (``--segment-chunks``; its three launches together make the step).
-``kda_fwd`` runs the chunked kernel, or for decode-shaped workloads (at most
-16 tokens per sequence) the recurrent one; ``config.kernel`` names it.  The default
-workload is the large throughput case: B=8, T=16384, H=32, K=V=128,
-lower_bound=-5, scale=1/sqrt(128), fp32 final_state written, no initial
-state.  Prints one JSON line:
+``kda_fwd`` runs the pipelined chunked kernel, or for decode-shaped
+workloads (at most 16 tokens per sequence) the recurrent or single-chunk
+one; ``config.kernel`` names it.
+
+The headline workload is the large throughput case: B=8, T=16384, H=32,
+K=V=128, lower_bound=-5, scale=1/sqrt(128), fp32 final_state written, no
+initial state, timed back to back.  By default the same run then measures
+the four other configured workloads (tiny B1 T64 H2, small B2 T128 H8, long
+B1 T8192 H16 with fp32 states, packed varlen N8 H32 with bf16 states), each
+with the cache flushed before every launch (they fit in, or overlap, the
+256 MiB MALL), and reports them under ``configs``.  Prints one JSON line:
 
   value     head-tokens/s of the whole job (B*T*H per step / seconds per step)
   roofline  the kernel against HBM: algorithmic bytes per launch (inputs read
@@ -17,17 +23,21 @@ state.  Prints one JSON line:
   cpu_baseline  the fp64 CPU oracle timed on this host on a bounded sample of
             the same workload (whole sequences of two batch rows), and on one
             thread over two chains
+  configs   per other workload: kernel ms, roofline fraction, head-tokens/s
+            and the oracle's head-tokens/s on the same inputs (all chains)
   copy_gbs  a plain 1 GiB device-to-device copy on the same GPU, for context
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--segment-chunks auto|off|N] [--flush-cache]
+                       [--headline-only] [--segment-chunks auto|off|N]
+                       [--flush-cache] [--kernel K] [--inverse I] [--sigmoid S]
 
---flush-cache reads a 512 MiB buffer before every launch (outside its HIP
-events), so that no launch finds its inputs in L2 or the 256 MiB MALL (a read
-leaves clean lines, so the launch pays no write-back for the flush); the
-step time is then the mean of the per-launch event times instead of the wall
-clock over the timed steps.  Small workloads (the decode ones) are measured
-this way too.
+--flush-cache reads a 512 MiB buffer before every launch of the headline
+(outside its HIP events), so that no launch finds its inputs in L2 or the
+256 MiB MALL (a read leaves clean lines, so the launch pays no write-back for
+the flush); the step time is then the mean of the per-launch event times
+instead of the wall clock over the timed steps.  The other configs are always
+measured this way.  --kernel, --inverse and --sigmoid pass the library's
+options (the kernel and the two ablations) for the headline workload.
 """
 from __future__ import annotations
 
@@ -46,6 +56,12 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
 # (A, P, W, U~, P U) + K V (decay) + C^3 (inverse) = 1,921,024.
 FLOPS_PER_HEAD_TOKEN = 1921024 / 16
 PROFILES = os.path.join(HERE, "profiles")
+HEADLINE = "large_b8_t16384_h32"
+OTHER_CONFIGS = ("tiny_b1_t64_h2", "small_b2_t128_h8", "long_b1_t8192_h16_state",
+                 "varlen_n8_h32_bf16state")
+# Host threads for the oracle: the host share of one GPU on this machine
+# (16 cores), whatever the affinity mask shows.
+ORACLE_THREADS_MAX = 16
 
 
 def source_digest() -> str:
@@ -90,13 +106,19 @@ def stored_traffic(workload: str, kernel: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(x, rows: int = 2):
-    """Time the oracle on whole sequences of the first `rows` batch rows."""
-    import torch
+def oracle_threads() -> int:
+    return min(ORACLE_THREADS_MAX, len(os.sched_getaffinity(0)))
+
+
+def cpu_baseline(x, rows=None, one_thread=True):
+    """Time the oracle on whole sequences: every sequence (rows=None) or the
+    first `rows` batch rows; all heads."""
     from oracle import kda_oracle
     B, T, H, _ = x.q.shape
-    rows = min(rows, B) if x.cu_seqlens is None else 1
-    cores = min(16, len(os.sched_getaffinity(0)))
+    if x.cu_seqlens is not None or rows is None:
+        rows = B
+    rows = min(rows, B)
+    cores = oracle_threads()
     sl = slice(0, rows)
     cpu = lambda t: None if t is None else t.cpu()
     q, k, v, g, beta = (cpu(t[sl]) for t in (x.q, x.k, x.v, x.g, x.beta))
@@ -110,18 +132,82 @@ def cpu_baseline(x, rows: int = 2):
     kda_oracle(*args, initial_state=init, cu_seqlens=cu, chains=chains, threads=cores)
     dt = time.perf_counter() - t0
     head_tokens = rows * T * H
-    # one thread, two chains of the first sequence
+    res = {"value": head_tokens / dt, "unit": "head-tokens/s", "cores": cores, "kind": "oracle",
+           "affinity_cores": len(os.sched_getaffinity(0)),
+           "sample": f"{len(chains)} whole (sequence, head) chains = {head_tokens} head-tokens "
+                     f"({rows} of {B} batch rows, all {H} heads), fp64 token loop on {cores} "
+                     f"threads, {dt:.2f} s wall"}
+    if one_thread:
+        t0 = time.perf_counter()
+        kda_oracle(*args, initial_state=init, cu_seqlens=cu, chains=chains[:2], threads=1)
+        dt1 = time.perf_counter() - t0
+        seq_len = T if cu is None else int(cu[1] - cu[0])
+        res["value_1thread"] = 2 * seq_len / dt1
+        res["sample_1thread"] = (f"chains (0,0), (0,1) = {2 * seq_len} head-tokens on one thread, "
+                                 f"{dt1:.2f} s wall")
+    return res
+
+
+def measure(kda, x, final_dtype, steps, warmup, flush, seg, opts):
+    """Warm up, then time `steps` calls; returns (ms_per_step, mean launch ms).
+
+    Per-launch HIP events on the launch stream give the kernel time.  With
+    `flush` (a 512 MiB device buffer) it is read before every launch, outside
+    the events, and the step time is the mean launch time; otherwise the
+    steps run back to back and the step time is the wall clock over them."""
+    import torch
+    H = x.q.shape[2]
+    out = torch.empty_like(x.v)
+    final = None
+    if final_dtype is not None:
+        final = torch.empty(x.num_seqs, H, 128, 128, dtype=final_dtype, device="cuda")
+
+    def step():
+        kda.fwd(x.q, x.k, x.v, x.g, x.beta, x.scale, out, x.A_log, x.dt_bias, x.lower_bound,
+                initial_state=x.initial_state, final_state=final, cu_seqlens=x.cu_seqlens,
+                check_cu_seqlens=False, segment_chunks=seg, **opts)
+
+    for _ in range(warmup):
+        if flush is not None:
+            flush.max()
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    kda_oracle(*args, initial_state=init, cu_seqlens=cu, chains=chains[:2], threads=1)
-    dt1 = time.perf_counter() - t0
-    seq_len = T if cu is None else int(cu[1] - cu[0])
-    return {"value": head_tokens / dt, "unit": "head-tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{len(chains)} whole (sequence, head) chains = {head_tokens} head-tokens "
-                      f"({rows} of {B} batch rows, all {H} heads), fp64 token loop, "
-                      f"{dt:.2f} s wall",
-            "value_1thread": 2 * seq_len / dt1,
-            "sample_1thread": f"chains (0,0), (0,1) = {2 * seq_len} head-tokens on one thread, "
-                              f"{dt1:.2f} s wall"}
+    for s, e in ev:
+        if flush is not None:
+            flush.max()
+        s.record(stream)
+        step()
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s.elapsed_time(e) for s, e in ev]
+    mean_launch = sum(launch_ms) / len(launch_ms)
+    # with cache flushes in between, the wall clock would count them: use the launches
+    ms_per_step = mean_launch if flush is not None else wall * 1e3 / steps
+    return ms_per_step, mean_launch
+
+
+def roofline_of(x, final_dtype, launch_ms, traffic=None):
+    B, T, H, _ = x.q.shape
+    launch_bytes = algorithmic_bytes(x, final_dtype)
+    achieved = launch_bytes / (launch_ms / 1e3) / 1e9
+    flops = B * T * H * FLOPS_PER_HEAD_TOKEN
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel_ms": round(launch_ms, 4), "bytes_per_launch": launch_bytes,
+            "flops_per_launch": round(flops),
+            "mfma_frac": round(flops / (launch_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
+def segment_choice(kda, x, arg):
+    if arg == "auto":
+        return kda.auto_segment_chunks(x.num_seqs * x.q.shape[2], x.q.shape[1])
+    return None if arg == "off" else int(arg)
 
 
 def main():
@@ -130,13 +216,19 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     # the clocks take some 25 launches (about 40 ms) to settle under this load
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--workload", default="large_b8_t16384_h32")
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--headline-only", action="store_true",
+                    help="measure only --workload (no other configs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--segment-chunks", default="auto",
                     help="segmented form: 'auto' (used only for workloads with few chains), "
                          "'off', or a segment length in 16-token chunks")
     ap.add_argument("--flush-cache", action="store_true",
-                    help="read a 512 MiB buffer before every launch (outside its timing)")
+                    help="read a 512 MiB buffer before every launch of --workload (outside "
+                         "its timing)")
+    ap.add_argument("--kernel", default=None, help="kda options: auto, mfma, recurrent, single")
+    ap.add_argument("--inverse", default=None, help="kda options: substitution, neumann")
+    ap.add_argument("--sigmoid", default=None, help="kda options: exp2, tanh")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="before warm-up, run one plain device-to-device copy of this many "
                          "bytes (untimed), as a known-size reference for HBM byte counters")
@@ -152,14 +244,12 @@ def main():
     from gated_delta_rule_36_amd import synth
 
     torch.cuda.set_device(0)
+    opts = {k: v for k, v in (("kernel", args.kernel), ("inverse", args.inverse),
+                              ("sigmoid", args.sigmoid)) if v is not None}
     print(f"[bench] drawing {args.workload} on the GPU", file=sys.stderr, flush=True)
     x = synth.workload(args.workload, device="cuda")
     B, T, H, K = x.q.shape
     final_dtype = x.final_dtype
-    out = torch.empty_like(x.v)
-    final = None
-    if final_dtype is not None:
-        final = torch.empty(x.num_seqs, H, 128, 128, dtype=final_dtype, device="cuda")
     torch.cuda.synchronize()
     if args.copy_bytes > 0:
         src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda")
@@ -167,7 +257,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    # context: a plain device-to-device copy of 1 GiB (read + write), best of 3
+    # context: a plain device-to-device copy of 1 GiB (read + write), best of 4
     src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     best = None
@@ -181,58 +271,17 @@ def main():
         best = ms if best is None else min(best, ms)
     copy_gbs = 2 * (1 << 30) / (best / 1e3) / 1e9
     del src, dst
-    flush = torch.ones(512 << 20, dtype=torch.uint8, device="cuda") if args.flush_cache else None
+    flush_buf = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
 
-    if args.segment_chunks == "auto":
-        seg = kda.auto_segment_chunks(x.num_seqs * H, T)
-    elif args.segment_chunks == "off":
-        seg = None
-    else:
-        seg = int(args.segment_chunks)
-
-    def step():
-        kda.fwd(x.q, x.k, x.v, x.g, x.beta, x.scale, out, x.A_log, x.dt_bias, x.lower_bound,
-                initial_state=x.initial_state, final_state=final, cu_seqlens=x.cu_seqlens,
-                check_cu_seqlens=False, segment_chunks=seg)
-
-    for _ in range(args.warmup):
-        if flush is not None:
-            flush.max()
-        step()
-    torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
-
-    stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s, e in ev:
-        if flush is not None:
-            flush.max()
-        s.record(stream)
-        step()
-        e.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    launch_ms = [s.elapsed_time(e) for s, e in ev]
-    # with cache flushes in between, the wall clock would count them: use the launches
-    ms_per_step = sum(launch_ms) / len(launch_ms) if flush is not None else wall * 1e3 / args.steps
+    seg = segment_choice(kda, x, args.segment_chunks)
+    ms_per_step, launch_ms = measure(kda, x, final_dtype, args.steps, args.warmup,
+                                     flush_buf if args.flush_cache else None, seg, opts)
     head_tokens = B * T * H
-    print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr,
-          flush=True)
-
-    avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
-    launch_bytes = algorithmic_bytes(x, final_dtype)
-    achieved = launch_bytes / avg_launch_s / 1e9
-    kernel = "mfma (segmented)" if seg else kda.fwd_kernel(T, x.cu_seqlens is not None)
-    traffic = stored_traffic(args.workload, kernel)
-    flops = head_tokens * FLOPS_PER_HEAD_TOKEN
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel_ms": round(avg_launch_s * 1e3, 4), "bytes_per_launch": launch_bytes,
-                "flops_per_launch": round(flops),
-                "mfma_frac": round(flops / avg_launch_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    print(f"[bench] {args.workload}: {args.warmup} warm-up + {args.steps} timed steps, "
+          f"{ms_per_step:.4f} ms/step", file=sys.stderr, flush=True)
+    kernel = "mfma (segmented)" if seg else kda.fwd_kernel(T, x.cu_seqlens is not None, **opts)
+    roofline = roofline_of(x, final_dtype, launch_ms,
+                           None if opts else stored_traffic(args.workload, kernel))
 
     result = {
         "metric": "KDA fwd head-tokens/sec (K=V=128); % of HBM/MFMA roofline",
@@ -251,15 +300,43 @@ def main():
                    "lower_bound": x.lower_bound, "varlen": x.cu_seqlens is not None,
                    "initial_state": None if x.initial_state is None else str(x.initial_state.dtype),
                    "final_state": None if final_dtype is None else str(final_dtype),
-                   "segment_chunks": seg,
-                   "kernel": kernel},
+                   "segment_chunks": seg, "kernel": kernel, **opts},
         "roofline": roofline,
         "copy_gbs": round(copy_gbs, 1),
-        "cache_flushed": flush is not None,
+        "cache_flushed": bool(args.flush_cache),
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(x)
+        result["cpu_baseline"] = cpu_baseline(x, rows=2)
+    del x
+
+    if not args.headline_only:
+        configs = {}
+        for name in OTHER_CONFIGS:
+            if name == args.workload:
+                continue
+            y = synth.workload(name, device="cuda")
+            yB, yT, yH, _ = y.q.shape
+            yseg = segment_choice(kda, y, "auto")
+            step_ms, lms = measure(kda, y, y.final_dtype, args.steps, args.warmup, flush_buf, yseg, {})
+            rl = roofline_of(y, y.final_dtype, lms)
+            ht = yB * yT * yH
+            entry = {"workload": name, "B": yB, "T": yT, "H": yH, "lower_bound": y.lower_bound,
+                     "varlen": y.cu_seqlens is not None,
+                     "initial_state": None if y.initial_state is None else str(y.initial_state.dtype),
+                     "final_state": None if y.final_dtype is None else str(y.final_dtype),
+                     "kernel": "mfma (segmented)" if yseg else kda.fwd_kernel(yT, y.cu_seqlens is not None),
+                     "segment_chunks": yseg, "cache_flushed": True, "head_tokens": ht,
+                     "ms_per_step": round(step_ms, 4), "head_tokens_per_s": ht / (step_ms / 1e3),
+                     "kernel_ms": rl["kernel_ms"], "frac": rl["frac"], "achieved_gbs": rl["achieved"],
+                     "bytes_per_launch": rl["bytes_per_launch"]}
+            print(f"[bench] {name}: {step_ms:.4f} ms/step, frac {rl['frac']}", file=sys.stderr,
+                  flush=True)
+            if not args.no_cpu_baseline:
+                entry["cpu_baseline"] = cpu_baseline(y, rows=None, one_thread=False)
+            configs[name] = entry
+            del y
+        result["configs"] = configs
     print(json.dumps(result), flush=True)
 
 

@@ -7,9 +7,9 @@ import os
 LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
 # Every symbol include/kda.h declares.
-EXPORTS = ("kda_fwd", "kda_fwd_scan", "kda_fwd_scan_workspace_bytes", "kda_status_string",
-           "kda_fwd_kernel", "kda_abi_version")
-ABI_VERSION = 3
+EXPORTS = ("kda_fwd", "kda_fwd_ex", "kda_fwd_scan", "kda_fwd_scan_workspace_bytes",
+           "kda_status_string", "kda_fwd_kernel", "kda_abi_version")
+ABI_VERSION = 4
 
 # kda_status codes (include/kda.h)
 KDA_OK = 0
@@ -24,11 +24,23 @@ KDA_ERR_SCALE = 8
 KDA_ERR_LAUNCH = 9
 KDA_ERR_WORKSPACE = 10
 KDA_ERR_ALIGNMENT = 11
+KDA_ERR_OPTION = 12
 
 # kda_dtype codes
 KDA_DTYPE_NONE = 0
 KDA_DTYPE_BF16 = 1
 KDA_DTYPE_FP32 = 2
+
+# kda_options fields
+KDA_KERNEL_AUTO, KDA_KERNEL_CHUNKED, KDA_KERNEL_RECURRENT, KDA_KERNEL_SINGLE = 0, 1, 2, 3
+KDA_INVERSE_SUBSTITUTION, KDA_INVERSE_NEUMANN = 0, 1
+KDA_SIGMOID_EXP2, KDA_SIGMOID_TANH = 0, 1
+
+
+class Options(ctypes.Structure):
+    """struct kda_options"""
+    _fields_ = [("kernel", ctypes.c_int32), ("inverse", ctypes.c_int32),
+                ("sigmoid", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class KdaLibraryMissing(RuntimeError):
@@ -51,14 +63,18 @@ def load() -> ctypes.CDLL:
     lib.kda_fwd.argtypes = [p, p, p, p, p, d, p, p, p, d, p, ctypes.c_int, p, ctypes.c_int,
                             p, i64, i64, i64, i64, i64, i64, p]
     lib.kda_fwd.restype = ctypes.c_int
+    opt = ctypes.POINTER(Options)
+    lib.kda_fwd_ex.argtypes = [p, p, p, p, p, d, p, p, p, d, p, ctypes.c_int, p, ctypes.c_int,
+                               p, i64, i64, i64, i64, i64, i64, opt, p]
+    lib.kda_fwd_ex.restype = ctypes.c_int
     lib.kda_fwd_scan.argtypes = [p, p, p, p, p, d, p, p, p, d, p, ctypes.c_int, p, ctypes.c_int,
-                                 p, i64, i64, i64, i64, i64, i64, i64, p, i64, p]
+                                 p, i64, i64, i64, i64, i64, i64, i64, p, i64, opt, p]
     lib.kda_fwd_scan.restype = ctypes.c_int
     lib.kda_fwd_scan_workspace_bytes.argtypes = [p, i64, i64, i64, i64, i64]
     lib.kda_fwd_scan_workspace_bytes.restype = i64
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
-    lib.kda_fwd_kernel.argtypes = [i64, ctypes.c_int]
+    lib.kda_fwd_kernel.argtypes = [i64, ctypes.c_int, opt]
     lib.kda_fwd_kernel.restype = ctypes.c_char_p
     lib.kda_abi_version.argtypes = []
     lib.kda_abi_version.restype = ctypes.c_int

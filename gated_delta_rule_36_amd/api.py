@@ -12,6 +12,7 @@ and ``dt_bias [H,128]``, ``lower_bound`` in [-5, 0], optional bf16/fp32
 """
 from __future__ import annotations
 
+import ctypes
 from typing import Optional, Union
 
 import torch
@@ -19,6 +20,23 @@ import torch
 from . import _lib
 
 _STATE_CODES = {torch.bfloat16: _lib.KDA_DTYPE_BF16, torch.float32: _lib.KDA_DTYPE_FP32}
+_KERNELS = {None: _lib.KDA_KERNEL_AUTO, "auto": _lib.KDA_KERNEL_AUTO, "mfma": _lib.KDA_KERNEL_CHUNKED,
+            "chunked": _lib.KDA_KERNEL_CHUNKED, "recurrent": _lib.KDA_KERNEL_RECURRENT,
+            "single": _lib.KDA_KERNEL_SINGLE}
+_INVERSES = {None: _lib.KDA_INVERSE_SUBSTITUTION, "substitution": _lib.KDA_INVERSE_SUBSTITUTION,
+             "neumann": _lib.KDA_INVERSE_NEUMANN}
+_SIGMOIDS = {None: _lib.KDA_SIGMOID_EXP2, "exp2": _lib.KDA_SIGMOID_EXP2, "tanh": _lib.KDA_SIGMOID_TANH}
+
+
+def _options(kernel, inverse, sigmoid):
+    """struct kda_options for the keyword choices, or None for all defaults."""
+    if kernel is None and inverse is None and sigmoid is None:
+        return None
+    for name, value, table in (("kernel", kernel, _KERNELS), ("inverse", inverse, _INVERSES),
+                               ("sigmoid", sigmoid, _SIGMOIDS)):
+        if value not in table:
+            raise ValueError(f"{name} must be one of {sorted(k for k in table if k)}, got {value!r}")
+    return _lib.Options(_KERNELS[kernel], _INVERSES[inverse], _SIGMOIDS[sigmoid], 0)
 
 
 class KdaError(RuntimeError):
@@ -59,7 +77,9 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
         final_state: Optional[torch.Tensor] = None,
         cu_seqlens: Optional[torch.Tensor] = None, *,
         check_cu_seqlens: bool = True,
-        segment_chunks: Union[None, int, str] = None) -> torch.Tensor:
+        segment_chunks: Union[None, int, str] = None,
+        kernel: Optional[str] = None, inverse: Optional[str] = None,
+        sigmoid: Optional[str] = None) -> torch.Tensor:
     """Run the chunked KDA forward pass; writes ``out`` (and ``final_state``).
 
     Enqueued on the current stream of ``q``'s device; returns ``out``.
@@ -73,6 +93,12 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
     (sequence, head) chains; ``"auto"`` picks a segment length from the
     sizes (:func:`auto_segment_chunks`), ``None`` runs ``kda_fwd``.  The
     workspace is a temporary allocation on the same stream.
+
+    ``kernel`` ("auto", "mfma", "recurrent", "single"), ``inverse``
+    ("substitution", "neumann") and ``sigmoid`` ("exp2", "tanh") fill the
+    library's ``kda_options`` (``None``: the default); they choose how the
+    same result is computed.  A combination no kernel implements for the call
+    raises :class:`KdaArgumentError`.
     """
     if not isinstance(q, torch.Tensor):
         raise TypeError("q must be a torch.Tensor")
@@ -141,6 +167,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
                                          or isinstance(segment_chunks, bool) or segment_chunks < 1):
         raise ValueError(f"segment_chunks must be a positive int, 'auto' or None, got {segment_chunks!r}")
 
+    opts = _options(kernel, inverse, sigmoid)
+    opts_ref = None if opts is None else ctypes.byref(opts)
     lib = _lib.load()
     with torch.cuda.device(device):
         stream = torch.cuda.current_stream(device).cuda_stream
@@ -149,7 +177,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
                 _ptr(initial_state), codes[0], _ptr(final_state), codes[1],
                 _ptr(cu_seqlens), num_seqs, B, T, H, K, V)
         if segment_chunks is None:
-            status = lib.kda_fwd(*args, stream)
+            status = lib.kda_fwd_ex(*args, opts_ref, stream)
         else:
             nbytes = lib.kda_fwd_scan_workspace_bytes(_ptr(cu_seqlens), num_seqs, B, T, H,
                                                       segment_chunks)
@@ -158,7 +186,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
             # freed right after the call: the caching allocator hands it out
             # again only to work ordered after this call on the same stream
             workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
-            status = lib.kda_fwd_scan(*args, segment_chunks, workspace.data_ptr(), nbytes, stream)
+            status = lib.kda_fwd_scan(*args, segment_chunks, workspace.data_ptr(), nbytes, opts_ref,
+                                      stream)
     if status != _lib.KDA_OK:
         if status == _lib.KDA_ERR_LAUNCH:
             raise KdaError(status)
@@ -166,12 +195,20 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
     return out
 
 
-def fwd_kernel(T: int, varlen: bool = False) -> str:
+def fwd_kernel(T: int, varlen: bool = False, *, kernel: Optional[str] = None,
+               inverse: Optional[str] = None, sigmoid: Optional[str] = None) -> str:
     """Name of the kernel ``fwd`` runs for a call with ``T`` tokens per batch
-    row (``varlen``: cu_seqlens given), as the library decides it (including
-    the KDA_KERNEL override): "recurrent", "single", "mfma" or "simt".  The segmented
-    form (``segment_chunks``) always runs the chunked kernel."""
-    return _lib.load().kda_fwd_kernel(int(T), 1 if varlen else 0).decode()
+    row (``varlen``: cu_seqlens given) and these options, as the library
+    decides it: "recurrent", "single" or "mfma".  Raises ValueError when the
+    options are invalid for such a call.  The segmented form
+    (``segment_chunks``) always runs the chunked kernel."""
+    opts = _options(kernel, inverse, sigmoid)
+    name = _lib.load().kda_fwd_kernel(int(T), 1 if varlen else 0,
+                                      None if opts is None else ctypes.byref(opts))
+    if name is None:
+        raise ValueError(f"no kernel implements kernel={kernel!r}, inverse={inverse!r}, "
+                         f"sigmoid={sigmoid!r} for T={T}, varlen={varlen}")
+    return name.decode()
 
 
 def auto_segment_chunks(chains: int, T: int, target_blocks: int = 256,

@@ -5,8 +5,6 @@
 
 #include <cmath>
 #include <cstdint>
-#include <cstdlib>
-#include <cstring>
 
 #include "kda_internal.h"
 
@@ -135,10 +133,46 @@ kda_status check_args(const void *q, const void *k, const void *v, const void *g
     // The gate is carried in log2 units so that every decay is a plain exp2
     // (lower_bound page, "Conversion to the Gate Scale Factor").
     p.gate_scale = static_cast<float>(lower_bound * kLog2e);
-    p.inverse = kda::inverse_from_env();
-    p.sigmoid = kda::sigmoid_from_env();
     c->chains = chains;
     return KDA_OK;
+}
+
+// The kernel a kda_fwd_ex call with these options runs (kda::Kernel), or -1
+// when the options are invalid for the call: an unknown value, a non-zero
+// reserved field, or a combination no kernel implements.  Decode-shaped
+// calls (no cu_seqlens, at most one chunk per sequence) go to the token
+// recurrence up to kRecurrentMaxTokens tokens and to the single-chunk kernel
+// up to 16; the rest to the pipelined chunked kernel.  The Neumann inverse
+// exists in the chunked kernel only; the tanh-form sigmoid in the chunked
+// (forward substitution) and single-chunk kernels.
+int choose_kernel(const kda_options *options, int64_t T, bool varlen)
+{
+    const kda_options none = {KDA_KERNEL_AUTO, KDA_INVERSE_SUBSTITUTION, KDA_SIGMOID_EXP2, 0};
+    const kda_options &o = options ? *options : none;
+    if (o.reserved != 0 || (o.inverse != KDA_INVERSE_SUBSTITUTION && o.inverse != KDA_INVERSE_NEUMANN) ||
+        (o.sigmoid != KDA_SIGMOID_EXP2 && o.sigmoid != KDA_SIGMOID_TANH))
+        return -1;
+    const bool neumann = o.inverse == KDA_INVERSE_NEUMANN, tanh_form = o.sigmoid == KDA_SIGMOID_TANH;
+    if (neumann && tanh_form)
+        return -1;
+    const bool one_chunk = !varlen && T <= kda::kChunk;
+    const bool recurrent_ok = !neumann && !tanh_form, single_ok = one_chunk && !neumann;
+    switch (o.kernel) {
+    case KDA_KERNEL_AUTO:
+        if (recurrent_ok && !varlen && T <= kda::kRecurrentMaxTokens)
+            return kda::kKernelRecurrent;
+        return single_ok ? kda::kKernelSingle : kda::kKernelChunked;
+    case KDA_KERNEL_CHUNKED: return kda::kKernelChunked;
+    case KDA_KERNEL_RECURRENT: return recurrent_ok ? kda::kKernelRecurrent : -1;
+    case KDA_KERNEL_SINGLE: return single_ok ? kda::kKernelSingle : -1;
+    default: return -1;
+    }
+}
+
+void apply_forms(const kda_options *options, kda::FwdParams *p)
+{
+    p->inverse = options && options->inverse == KDA_INVERSE_NEUMANN ? kda::kInverseNeumann : kda::kInverseSubst;
+    p->sigmoid = options && options->sigmoid == KDA_SIGMOID_TANH ? kda::kSigmoidTanh : kda::kSigmoidExp;
 }
 
 // Segments per chain for segments of seg_chunks chunks: every sequence has
@@ -155,6 +189,31 @@ constexpr int64_t kSlabBytes = int64_t(kda::kHeadDim) * kda::kHeadDim * 4;  // o
 
 }  // namespace
 
+extern "C" kda_status kda_fwd_ex(const void *q, const void *k, const void *v, const void *g,
+                                 const void *beta, double scale, void *out, const float *A_log,
+                                 const float *dt_bias, double lower_bound,
+                                 const void *initial_state, kda_dtype initial_state_dtype,
+                                 void *final_state, kda_dtype final_state_dtype,
+                                 const int64_t *cu_seqlens, int64_t num_seqs, int64_t B,
+                                 int64_t T, int64_t H, int64_t K, int64_t V,
+                                 const kda_options *options, void *stream)
+{
+    Checked c;
+    const kda_status st = check_args(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
+                                     initial_state, initial_state_dtype, final_state,
+                                     final_state_dtype, cu_seqlens, num_seqs, B, T, H, K, V, &c);
+    if (st != KDA_OK)
+        return st;
+    const int kernel = choose_kernel(options, T, cu_seqlens != nullptr);
+    if (kernel < 0)
+        return KDA_ERR_OPTION;
+    apply_forms(options, &c.p);
+    if (c.chains == 0)
+        return KDA_OK;
+    hipError_t err = kda::launch_forward(c.p, kernel, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
 extern "C" kda_status kda_fwd(const void *q, const void *k, const void *v, const void *g,
                               const void *beta, double scale, void *out, const float *A_log,
                               const float *dt_bias, double lower_bound,
@@ -163,16 +222,9 @@ extern "C" kda_status kda_fwd(const void *q, const void *k, const void *v, const
                               const int64_t *cu_seqlens, int64_t num_seqs, int64_t B,
                               int64_t T, int64_t H, int64_t K, int64_t V, void *stream)
 {
-    Checked c;
-    const kda_status st = check_args(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
-                                     initial_state, initial_state_dtype, final_state,
-                                     final_state_dtype, cu_seqlens, num_seqs, B, T, H, K, V, &c);
-    if (st != KDA_OK)
-        return st;
-    if (c.chains == 0)
-        return KDA_OK;
-    hipError_t err = kda::launch_forward(c.p, static_cast<hipStream_t>(stream));
-    return err == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+    return kda_fwd_ex(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+                      initial_state_dtype, final_state, final_state_dtype, cu_seqlens, num_seqs, B,
+                      T, H, K, V, nullptr, stream);
 }
 
 extern "C" int64_t kda_fwd_scan_workspace_bytes(const int64_t *cu_seqlens, int64_t num_seqs,
@@ -188,14 +240,16 @@ extern "C" int64_t kda_fwd_scan_workspace_bytes(const int64_t *cu_seqlens, int64
     return bytes;
 }
 
-extern "C" kda_status kda_fwd_scan(const void *q, const void *k, const void *v, const void *g,
-                                   const void *beta, double scale, void *out, const float *A_log,
-                                   const float *dt_bias, double lower_bound,
-                                   const void *initial_state, kda_dtype initial_state_dtype,
-                                   void *final_state, kda_dtype final_state_dtype,
-                                   const int64_t *cu_seqlens, int64_t num_seqs, int64_t B,
-                                   int64_t T, int64_t H, int64_t K, int64_t V, int64_t seg_chunks,
-                                   void *workspace, int64_t workspace_bytes, void *stream)
+namespace {
+
+// kda_fwd_scan's checks and launch.
+kda_status fwd_scan(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                    double scale, void *out, const float *A_log, const float *dt_bias,
+                    double lower_bound, const void *initial_state, kda_dtype initial_state_dtype,
+                    void *final_state, kda_dtype final_state_dtype, const int64_t *cu_seqlens,
+                    int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+                    int64_t seg_chunks, void *workspace, int64_t workspace_bytes,
+                    const kda_options *options, void *stream)
 {
     Checked c;
     const kda_status st = check_args(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
@@ -203,6 +257,12 @@ extern "C" kda_status kda_fwd_scan(const void *q, const void *k, const void *v, 
                                      final_state_dtype, cu_seqlens, num_seqs, B, T, H, K, V, &c);
     if (st != KDA_OK)
         return st;
+    // the segmented form runs the pipelined chunked kernel (exp2 sigmoid)
+    if (options && ((options->kernel != KDA_KERNEL_AUTO && options->kernel != KDA_KERNEL_CHUNKED) ||
+                    options->sigmoid != KDA_SIGMOID_EXP2 ||
+                    choose_kernel(options, T, cu_seqlens != nullptr) < 0))
+        return KDA_ERR_OPTION;
+    apply_forms(options, &c.p);
     const int64_t n_seg = segments_per_chain(T, seg_chunks);
     int64_t blocks;
     // grids: chains * n_seg blocks for the map and output passes, chains * 8
@@ -230,6 +290,23 @@ extern "C" kda_status kda_fwd_scan(const void *q, const void *k, const void *v, 
     return err == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
+}  // namespace
+
+extern "C" kda_status kda_fwd_scan(const void *q, const void *k, const void *v, const void *g,
+                                   const void *beta, double scale, void *out, const float *A_log,
+                                   const float *dt_bias, double lower_bound,
+                                   const void *initial_state, kda_dtype initial_state_dtype,
+                                   void *final_state, kda_dtype final_state_dtype,
+                                   const int64_t *cu_seqlens, int64_t num_seqs, int64_t B,
+                                   int64_t T, int64_t H, int64_t K, int64_t V, int64_t seg_chunks,
+                                   void *workspace, int64_t workspace_bytes,
+                                   const kda_options *options, void *stream)
+{
+    return fwd_scan(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+                    initial_state_dtype, final_state, final_state_dtype, cu_seqlens, num_seqs, B, T,
+                    H, K, V, seg_chunks, workspace, workspace_bytes, options, stream);
+}
+
 extern "C" const char *kda_status_string(kda_status status)
 {
     switch (status) {
@@ -245,6 +322,7 @@ extern "C" const char *kda_status_string(kda_status status)
     case KDA_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
     case KDA_ERR_WORKSPACE: return "workspace is NULL, not 16-byte aligned, too small, or overlaps a tensor";
     case KDA_ERR_ALIGNMENT: return "a tensor pointer is misaligned (q, k, v, g, out, states: 16 bytes; beta 2; A_log, dt_bias 4; cu_seqlens 8)";
+    case KDA_ERR_OPTION: return "invalid options: unknown value, non-zero reserved field, or a kernel / inverse / sigmoid combination not implemented for this call";
     }
     return "unknown status";
 }
@@ -252,56 +330,13 @@ extern "C" const char *kda_status_string(kda_status status)
 extern "C" int kda_abi_version(void) { return KDA_ABI_VERSION; }
 
 namespace kda {
-// Kernel choice, read at every call.  Calls without cu_seqlens of at most
-// one chunk per sequence are decode-shaped (the state traffic dominates): up
-// to kRecurrentMaxTokens tokens they take the recurrent kernel, up to 16 the
-// single-chunk kernel; everything else takes the pipelined chunked kernel.
-// KDA_KERNEL=mfma, =recurrent, =single (calls it can take; others fall back
-// to mfma) or =simt (the plain fp32 chunked kernel, for cross-checks) forces
-// the choice for every call.
-enum KernelChoice { kKernelMfma, kKernelRecurrent, kKernelSingle, kKernelSimt };
-
-static KernelChoice kernel_choice(int64_t T, bool varlen)
+hipError_t launch_forward(const FwdParams &p, int kernel, hipStream_t stream)
 {
-    const char *e = std::getenv("KDA_KERNEL");
-    if (e && std::strcmp(e, "simt") == 0)
-        return kKernelSimt;
-    if (e && std::strcmp(e, "recurrent") == 0)
-        return kKernelRecurrent;
-    if (e && std::strcmp(e, "mfma") == 0)
-        return kKernelMfma;
-    const bool one_chunk = !varlen && T <= kChunk;  // what the single-chunk kernel takes
-    if (e && std::strcmp(e, "single") == 0)
-        return one_chunk ? kKernelSingle : kKernelMfma;
-    if (!varlen && T <= kRecurrentMaxTokens)
-        return kKernelRecurrent;
-    return one_chunk ? kKernelSingle : kKernelMfma;
-}
-
-hipError_t launch_forward(const FwdParams &p, hipStream_t stream)
-{
-    switch (kernel_choice(p.T, p.cu_seqlens != nullptr)) {
-    case kKernelSimt: return launch_chunk_simt(p, stream);
+    switch (kernel) {
     case kKernelRecurrent: return launch_decode(p, stream);
     case kKernelSingle: return launch_chunk_single(p, stream);
     default: return launch_chunk_mfma(p, stream);
     }
-}
-
-// KDA_SIGMOID=tanh selects the rational-tanh form of the logistic function in
-// the MFMA kernel's gate (an ablation of the pages' choice); read at every call.
-int sigmoid_from_env()
-{
-    const char *e = std::getenv("KDA_SIGMOID");
-    return e && std::strcmp(e, "tanh") == 0 ? kSigmoidTanh : kSigmoidExp;
-}
-
-// KDA_INVERSE=neumann selects the fp16 Neumann-product inverse in the MFMA
-// kernel (an ablation of the pages' choice); read at every call.
-int inverse_from_env()
-{
-    const char *e = std::getenv("KDA_INVERSE");
-    return e && std::strcmp(e, "neumann") == 0 ? kInverseNeumann : kInverseSubst;
 }
 
 // The segmented form: map (end states and, with more than two segments,
@@ -322,12 +357,12 @@ hipError_t launch_forward_scan(const FwdParams &p, hipStream_t stream)
 }
 }  // namespace kda
 
-extern "C" const char *kda_fwd_kernel(int64_t T, int varlen)
+extern "C" const char *kda_fwd_kernel(int64_t T, int varlen, const kda_options *options)
 {
-    switch (kda::kernel_choice(T, varlen != 0)) {
-    case kda::kKernelSimt: return "simt";
+    switch (choose_kernel(options, T, varlen != 0)) {
     case kda::kKernelRecurrent: return "recurrent";
     case kda::kKernelSingle: return "single";
-    default: return "mfma";
+    case kda::kKernelChunked: return "mfma";
+    default: return nullptr;
     }
 }

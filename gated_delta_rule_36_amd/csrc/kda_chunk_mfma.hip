@@ -968,13 +968,22 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
         } else {
             // outputs of every segment from its true start state: the real
             // one for segment 0, seg_b[s - 1] (after the combine step) for
-            // the others; the chain's last segment writes the final state
+            // the others; the chain's last segment writes the final state.
+            // With two or more segments, segment 0 reads the copy of the
+            // initial state that the map pass left in its seg_m slab (which
+            // holds no matrix): final_state may be the initial_state buffer,
+            // and the last segment's workgroup may store it before segment
+            // 0's workgroup has started.
             if (seg >= segs)
                 return;
             if (seg > 0) {
                 src = kSrcFp32;
                 src_ptr = p.seg_b;
                 src_slab = scratch - D * D;
+            } else if (segs > 1 && src != kSrcZero) {
+                src = kSrcFp32;
+                src_ptr = p.seg_m;
+                src_slab = scratch;
             }
             if (seg != segs - 1)
                 dst = kDstNone;
@@ -1021,6 +1030,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
             }
         }
         sw.load_state(src, src_ptr, src_slab);
+        // map pass, segment 0: keep a copy of the chain's initial state (fp32)
+        // in the segment's seg_m slab for the output pass
+        if (p.phase != kPhaseWhole && p.phase != kPhaseOut && seg == 0 && src != kSrcZero)
+            sw.store_state(kDstFp32, p.seg_m, dst_slab);
         if (n_iter > 0)
             lds_barrier();  // the gate waves' first loads are in LDS
         state_loop<kFused ? kChunkState : MODE, PipeLayout>(sw, n_iter, nc);

@@ -13,11 +13,11 @@ constexpr int kHeadDim = 128;  // K = V = 128
 enum StateKind : int { kStateNone = 0, kStateBf16 = 1, kStateFp32 = 2 };
 enum Phase : int { kPhaseWhole = 0, kPhaseMapB = 1, kPhaseMapBM = 2, kPhaseOut = 3 };
 // How the MFMA kernel forms T = (I + A)^-1: fp32 forward substitution (the
-// default) or the fp16 Neumann product (KDA_INVERSE=neumann; an ablation).
+// default) or the fp16 Neumann product (an ablation; KDA_INVERSE_NEUMANN).
 enum Inverse : int { kInverseSubst = 0, kInverseNeumann = 1 };
-// How the MFMA kernel's gate evaluates the logistic function: 1/(1 + 2^-x')
-// with the hardware exp2 and rcp (the default), or 1/2 + tanh(x/2)/2 with a
-// rational tanh (KDA_SIGMOID=tanh; an ablation, whole-chain calls only).
+// How the gate evaluates the logistic function: 1/(1 + 2^-x') with the
+// hardware exp2 and rcp (the default), or 1/2 + tanh(x/2)/2 with a rational
+// tanh (an ablation; KDA_SIGMOID_TANH, whole-chain chunked calls only).
 enum Sigmoid : int { kSigmoidExp = 0, kSigmoidTanh = 1 };
 
 // Everything a launch needs.  Pointers are device pointers; sizes were
@@ -55,15 +55,12 @@ struct FwdParams {
     float *seg_m = nullptr;  // [chains][n_seg] fp32-sized slabs: M_s itself as bf16 hi, lo planes [K][K]
 };
 
-// Enqueue the whole forward pass on `stream`.  Returns the launch status.
-hipError_t launch_forward(const FwdParams &p, hipStream_t stream);
+// The kernels kda_fwd_ex chooses between.
+enum Kernel : int { kKernelChunked = 1, kKernelRecurrent = 2, kKernelSingle = 3 };
 
-// The inverse method the environment selects (KDA_INVERSE=neumann), read at
-// every call.
-int inverse_from_env();
-// The sigmoid form the environment selects (KDA_SIGMOID=tanh), read at every
-// call.
-int sigmoid_from_env();
+// Enqueue the whole forward pass on `stream` with kernel `kernel`.  Returns
+// the launch status.
+hipError_t launch_forward(const FwdParams &p, int kernel, hipStream_t stream);
 
 // Enqueue the segmented form: map (phase 1), combine, output (phase 3).
 // p.seg_chunks, p.n_seg, p.seg_b and p.seg_m must be set.
@@ -71,7 +68,6 @@ hipError_t launch_forward_scan(const FwdParams &p, hipStream_t stream);
 
 // Individual kernel launchers (one per implementation).
 hipError_t launch_chunk_mfma(const FwdParams &p, hipStream_t stream);
-hipError_t launch_chunk_simt(const FwdParams &p, hipStream_t stream);
 // The chunked stages for calls of at most one chunk (16 tokens) per sequence
 // and no cu_seqlens: one 4-wave workgroup per chain, several per compute unit.
 hipError_t launch_chunk_single(const FwdParams &p, hipStream_t stream);

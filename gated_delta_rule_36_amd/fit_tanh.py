@@ -1,5 +1,5 @@
 """Fit of the rational tanh used by the tanh form of the gate's logistic
-function (kda_chunk_mfma.hip, KDA_SIGMOID=tanh).
+function (kda_chunk_mfma.hip, the sigmoid="tanh" option).
 
 tanh(y) ~ y P(y^2) / Q(y^2) on 0 < y <= 9 with P and Q of degree 4 in y^2 and
 P(0) = Q(0) = 1 (tanh is odd and tanh(y) / y -> 1).  The coefficients come

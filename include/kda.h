@@ -29,9 +29,9 @@
  * Ownership and threading: the caller owns every buffer.  All tensor
  * pointers are DEVICE pointers to contiguous row-major memory on the current
  * HIP device.  The library allocates nothing, keeps no state between calls,
- * never synchronises and is safe to call from several host threads.  The
- * work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
- * and completes asynchronously.
+ * reads no environment variables, never synchronises and is safe to call
+ * from several host threads.  The work is enqueued on `stream` (a
+ * hipStream_t; NULL = the default stream) and completes asynchronously.
  */
 #ifndef KDA_H
 #define KDA_H
@@ -65,11 +65,15 @@ typedef enum kda_status {
                                   aligned, smaller than
                                   kda_fwd_scan_workspace_bytes(), or
                                   overlapping a tensor argument */
-    KDA_ERR_ALIGNMENT = 11     /* a non-NULL pointer is misaligned: q, k, v,
+    KDA_ERR_ALIGNMENT = 11,    /* a non-NULL pointer is misaligned: q, k, v,
                                   g, out, initial_state and final_state need
                                   16 bytes, beta 2, A_log and dt_bias 4,
                                   cu_seqlens 8 (allocator memory and whole
                                   token rows of it always are) */
+    KDA_ERR_OPTION = 12        /* kda_options: an unknown value, a non-zero
+                                  reserved field, or a kernel / inverse /
+                                  sigmoid combination that no kernel of the
+                                  library implements for this call */
 } kda_status;
 
 /* Element type of initial_state / final_state. */
@@ -78,6 +82,58 @@ typedef enum kda_dtype {
     KDA_DTYPE_BF16 = 1,
     KDA_DTYPE_FP32 = 2
 } kda_dtype;
+
+/*
+ * Explicit choices for kda_fwd_ex and kda_fwd_scan (a NULL options pointer
+ * means all defaults, which is what kda_fwd uses).  They change how the
+ * same result is computed, never what is computed: the kernel, and two of
+ * the pages' own design choices kept as ablations.
+ *
+ *   kernel   KDA_KERNEL_AUTO: decode-shaped calls (no cu_seqlens, at most
+ *            16 tokens), where the state traffic dominates, take the token
+ *            recurrence (at most 8 tokens) or the single-chunk kernel; all
+ *            other calls the pipelined chunked kernel.  CHUNKED, RECURRENT
+ *            and SINGLE force one kernel; SINGLE takes only calls without
+ *            cu_seqlens of at most 16 tokens.
+ *   inverse  how the chunked kernels form the unit lower-triangular 16x16
+ *            inverse (I + A)^-1: fp32 forward substitution (default), or the
+ *            fp16 Neumann-series product the chunk-size page describes under
+ *            "Efficient 16x16 Matrix Inversion" (pipelined chunked kernel
+ *            only).
+ *   sigmoid  how the gate evaluates the logistic function: 1/(1 + 2^-x') with
+ *            the hardware exp2 and reciprocal (default), or 1/2 + tanh(x/2)/2
+ *            with a rational tanh, the tanh form the lower_bound page names
+ *            (whole-chain calls of the chunked and single-chunk kernels,
+ *            forward substitution only).
+ *   reserved must be 0.
+ *
+ * With KDA_KERNEL_AUTO a non-default inverse or sigmoid restricts the choice
+ * to the kernels that implement it; a forced kernel that does not implement
+ * the requested combination, or cannot take the call, gives KDA_ERR_OPTION.
+ */
+typedef enum kda_kernel {
+    KDA_KERNEL_AUTO = 0,
+    KDA_KERNEL_CHUNKED = 1,
+    KDA_KERNEL_RECURRENT = 2,
+    KDA_KERNEL_SINGLE = 3
+} kda_kernel;
+
+typedef enum kda_inverse {
+    KDA_INVERSE_SUBSTITUTION = 0,
+    KDA_INVERSE_NEUMANN = 1
+} kda_inverse;
+
+typedef enum kda_sigmoid {
+    KDA_SIGMOID_EXP2 = 0,
+    KDA_SIGMOID_TANH = 1
+} kda_sigmoid;
+
+typedef struct kda_options {
+    int32_t kernel;   /* kda_kernel */
+    int32_t inverse;  /* kda_inverse */
+    int32_t sigmoid;  /* kda_sigmoid */
+    int32_t reserved; /* 0 */
+} kda_options;
 
 /*
  * kda_fwd - chunked KDA forward pass.
@@ -122,6 +178,20 @@ kda_status kda_fwd(const void *q, const void *k, const void *v, const void *g,
                    void *stream);
 
 /*
+ * kda_fwd_ex - kda_fwd with explicit options (NULL = the defaults, which is
+ * exactly kda_fwd).  Same arguments, results and errors as kda_fwd, plus
+ * KDA_ERR_OPTION.
+ */
+kda_status kda_fwd_ex(const void *q, const void *k, const void *v, const void *g,
+                      const void *beta, double scale, void *out,
+                      const float *A_log, const float *dt_bias, double lower_bound,
+                      const void *initial_state, kda_dtype initial_state_dtype,
+                      void *final_state, kda_dtype final_state_dtype,
+                      const int64_t *cu_seqlens, int64_t num_seqs,
+                      int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+                      const kda_options *options, void *stream);
+
+/*
  * kda_fwd_scan - the same forward pass as kda_fwd (same arguments, same
  * results up to rounding), computed with parallelism inside each sequence:
  * for workloads with few (sequence, head) chains, where kda_fwd leaves most
@@ -139,7 +209,9 @@ kda_status kda_fwd(const void *q, const void *k, const void *v, const void *g,
  * the combined states stay fp32; M and the running state enter the combine
  * as hi + lo bf16 pairs (about 17 significant bits each), so the results
  * match kda_fwd's to within the rounding of the bf16 matrix operands both
- * forms use.
+ * forms use.  The first pass also keeps a copy of each chain's initial
+ * state in the workspace, which the output pass reads: final_state may be
+ * the initial_state buffer here too.
  *
  *   seg_chunks       chunks per segment, >= 1 (KDA_ERR_SIZE otherwise).  One
  *                    segment per chain (seg_chunks >= ceil(T / 16)) is exactly
@@ -151,9 +223,12 @@ kda_status kda_fwd(const void *q, const void *k, const void *v, const void *g,
  *                    used by other work until the call's work has completed
  *                    on `stream`.
  *   workspace_bytes  its size in bytes.
+ *   options          as for kda_fwd_ex (NULL = defaults); the segmented
+ *                    form runs the pipelined chunked kernel, so the kernel
+ *                    must be AUTO or CHUNKED and the sigmoid EXP2
+ *                    (KDA_ERR_OPTION otherwise).
  * Every other argument, the ownership rules and the error codes are those of
- * kda_fwd, plus KDA_ERR_WORKSPACE.  The segmented form always runs on the
- * MFMA kernels.
+ * kda_fwd, plus KDA_ERR_WORKSPACE and KDA_ERR_OPTION.
  */
 kda_status kda_fwd_scan(const void *q, const void *k, const void *v, const void *g,
                         const void *beta, double scale, void *out,
@@ -163,7 +238,7 @@ kda_status kda_fwd_scan(const void *q, const void *k, const void *v, const void 
                         const int64_t *cu_seqlens, int64_t num_seqs,
                         int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
                         int64_t seg_chunks, void *workspace, int64_t workspace_bytes,
-                        void *stream);
+                        const kda_options *options, void *stream);
 
 /*
  * Bytes of workspace kda_fwd_scan needs for these sizes: two fp32 128x128
@@ -179,22 +254,19 @@ int64_t kda_fwd_scan_workspace_bytes(const int64_t *cu_seqlens, int64_t num_seqs
 const char *kda_status_string(kda_status status);
 
 /*
- * Name of the kernel kda_fwd runs for a call with T tokens per batch row
- * (varlen != 0: cu_seqlens given).  Decode-shaped calls (no cu_seqlens, at
- * most 16 tokens), where the state traffic dominates, take "recurrent" (the
- * token recurrence itself, T <= 8) or "single" (the chunked stages for one
- * chunk, 8 < T <= 16), each with one small workgroup per chain; everything
- * else takes "mfma", the pipelined chunked kernel.  The environment variable
- * KDA_KERNEL (mfma, recurrent, single, or simt: a plain fp32 chunked kernel
- * kept for cross-checks), read at every call, overrides the choice; single
- * applies only to calls it can take (no cu_seqlens, T <= 16) and falls back
- * to mfma otherwise.  Returns a static string; pure host logic, no device
- * work.  kda_fwd_scan always runs the chunked kernel.
+ * Name of the kernel kda_fwd_ex runs for a call with T tokens per batch row
+ * (varlen != 0: cu_seqlens given) and these options (NULL = defaults, i.e.
+ * kda_fwd's choice): "recurrent" (the token recurrence itself), "single"
+ * (the chunked stages for one chunk, one small workgroup per chain) or
+ * "mfma" (the pipelined chunked kernel); see kda_options.  Returns NULL when
+ * the options are invalid for such a call (kda_fwd_ex would return
+ * KDA_ERR_OPTION).  A static string; pure host logic, no device work.
+ * kda_fwd_scan always runs the chunked kernel.
  */
-const char *kda_fwd_kernel(int64_t T, int varlen);
+const char *kda_fwd_kernel(int64_t T, int varlen, const kda_options *options);
 
 /* ABI version of this header (bumped on any signature change). */
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 int kda_abi_version(void);
 
 #ifdef __cplusplus

@@ -67,10 +67,13 @@ def call(**over):
              init=None, init_dtype=0, final=None, final_dtype=0, cu=None, num_seqs=0,
              B=1, T=0, H=1, K=128, V=128)
     a.update(over)
-    return _lib.load().kda_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["scale"], a["out"],
-                               a["A_log"], a["dt_bias"], a["lower_bound"], a["init"],
-                               a["init_dtype"], a["final"], a["final_dtype"], a["cu"],
-                               a["num_seqs"], a["B"], a["T"], a["H"], a["K"], a["V"], None)
+    lib = _lib.load()
+    args = (a["q"], a["k"], a["v"], a["g"], a["beta"], a["scale"], a["out"], a["A_log"],
+            a["dt_bias"], a["lower_bound"], a["init"], a["init_dtype"], a["final"],
+            a["final_dtype"], a["cu"], a["num_seqs"], a["B"], a["T"], a["H"], a["K"], a["V"])
+    if "options" in a:
+        return lib.kda_fwd_ex(*args, a["options"], None)
+    return lib.kda_fwd(*args, None)
 
 
 # The dummy buffers are only 64 bytes, but the size checks use the declared
@@ -116,8 +119,8 @@ def test_argument_errors_are_reported_before_launch(over, code):
 
 
 def test_status_strings_are_distinct():
-    msgs = [_lib.status_string(c) for c in range(12)]
-    assert len(set(msgs)) == 12 and msgs[0] == "ok"
+    msgs = [_lib.status_string(c) for c in range(13)]
+    assert len(set(msgs)) == 13 and msgs[0] == "ok"
     assert _lib.status_string(123) == "unknown status"
 
 
@@ -158,7 +161,7 @@ def call_scan(seg=4, ws=None, ws_bytes=1 << 30, **over):
                                     a["A_log"], a["dt_bias"], a["lower_bound"], a["init"],
                                     a["init_dtype"], a["final"], a["final_dtype"], a["cu"],
                                     a["num_seqs"], a["B"], a["T"], a["H"], a["K"], a["V"],
-                                    seg, ws, ws_bytes, None)
+                                    seg, ws, ws_bytes, a.get("options"), None)
 
 
 # Every call fails on the planted error, so nothing is launched.
@@ -201,25 +204,93 @@ def test_auto_segment_chunks_policy():
     assert auto(0, 1000) is None
 
 
-def test_kernel_choice(monkeypatch):
+def _opts(kernel=0, inverse=0, sigmoid=0, reserved=0):
+    return ctypes.byref(_lib.Options(kernel, inverse, sigmoid, reserved))
+
+
+def test_kernel_choice():
     """Decode-shaped calls (no cu_seqlens, at most 16 tokens) take the
     recurrent kernel up to 8 tokens and the single-chunk kernel beyond,
-    everything else the pipelined chunked one; KDA_KERNEL overrides the
-    choice and is read at every call."""
-    monkeypatch.delenv("KDA_KERNEL", raising=False)
+    everything else the pipelined chunked one; the options force a kernel,
+    and restrict the automatic choice to the kernels that implement a
+    non-default inverse or sigmoid.  No environment variable is read."""
     choice = kda.fwd_kernel
     assert [choice(t) for t in (0, 1, 8)] == ["recurrent"] * 3
     assert [choice(t) for t in (9, 15, 16)] == ["single"] * 3
     assert [choice(t) for t in (17, 64, 16384)] == ["mfma"] * 3
     assert choice(1, varlen=True) == choice(16, varlen=True) == "mfma"
-    for forced in ("mfma", "recurrent", "simt"):
-        monkeypatch.setenv("KDA_KERNEL", forced)
-        assert choice(1) == choice(10000) == choice(5, varlen=True) == forced
-    monkeypatch.setenv("KDA_KERNEL", "single")
-    assert choice(0) == choice(16) == "single"
-    assert choice(17) == choice(5, varlen=True) == "mfma"
-    monkeypatch.setenv("KDA_KERNEL", "no-such-kernel")
-    assert choice(1) == "recurrent" and choice(12) == "single" and choice(17) == "mfma"
+    for forced in ("mfma", "recurrent"):
+        assert choice(1, kernel=forced) == choice(10000, kernel=forced) == \
+            choice(5, varlen=True, kernel=forced) == forced
+    assert choice(0, kernel="single") == choice(16, kernel="single") == "single"
+    for bad in (dict(T=17), dict(T=5, varlen=True)):
+        with pytest.raises(ValueError):
+            choice(kernel="single", **bad)
+    # the Neumann inverse exists in the chunked kernel only
+    assert choice(1, inverse="neumann") == choice(16, inverse="neumann") == "mfma"
+    with pytest.raises(ValueError):
+        choice(1, kernel="recurrent", inverse="neumann")
+    with pytest.raises(ValueError):
+        choice(12, kernel="single", inverse="neumann")
+    # the tanh-form sigmoid: single-chunk kernel for decode-shaped calls, else chunked
+    assert choice(3, sigmoid="tanh") == choice(16, sigmoid="tanh") == "single"
+    assert choice(17, sigmoid="tanh") == choice(3, varlen=True, sigmoid="tanh") == "mfma"
+    with pytest.raises(ValueError):
+        choice(3, kernel="recurrent", sigmoid="tanh")
+    with pytest.raises(ValueError):
+        choice(100, inverse="neumann", sigmoid="tanh")
+    with pytest.raises(ValueError):
+        choice(100, kernel="simt")
+
+
+def test_kernel_choice_ignores_the_environment(monkeypatch):
+    monkeypatch.setenv("KDA_KERNEL", "mfma")
+    monkeypatch.setenv("KDA_INVERSE", "neumann")
+    monkeypatch.setenv("KDA_SIGMOID", "tanh")
+    assert kda.fwd_kernel(1) == "recurrent" and kda.fwd_kernel(12) == "single"
+
+
+def test_kda_fwd_kernel_c_abi():
+    f = _lib.load().kda_fwd_kernel
+    assert f(5, 0, None) == b"recurrent" and f(5, 1, None) == b"mfma"
+    assert f(5, 0, _opts(kernel=_lib.KDA_KERNEL_SINGLE)) == b"single"
+    assert f(5, 0, _opts(kernel=9)) is None
+    assert f(5, 0, _opts(inverse=2)) is None
+    assert f(5, 0, _opts(sigmoid=-1)) is None
+    assert f(5, 0, _opts(reserved=1)) is None
+
+
+@pytest.mark.parametrize("opts", [dict(kernel=4), dict(inverse=7), dict(sigmoid=2), dict(reserved=3),
+                                  dict(kernel=_lib.KDA_KERNEL_RECURRENT, inverse=_lib.KDA_INVERSE_NEUMANN),
+                                  dict(kernel=_lib.KDA_KERNEL_SINGLE, inverse=_lib.KDA_INVERSE_NEUMANN),
+                                  dict(inverse=_lib.KDA_INVERSE_NEUMANN, sigmoid=_lib.KDA_SIGMOID_TANH)])
+def test_option_errors_are_reported_before_launch(opts):
+    assert call(options=_opts(**opts)) == _lib.KDA_ERR_OPTION
+    # and the argument checks still come first
+    assert call(options=_opts(**opts), K=64) == _lib.KDA_ERR_HEAD_DIM
+
+
+def test_default_options_equal_kda_fwd():
+    # packed mode with no sequence: every check passes and nothing is launched
+    none = dict(cu=ADDR[9], num_seqs=0)
+    assert call(options=None, **none) == call(options=_opts(), **none) == call(**none) == _lib.KDA_OK
+
+
+def test_scan_option_errors():
+    ws = dict(ws=BADDR[11])
+    for o in (dict(kernel=_lib.KDA_KERNEL_RECURRENT), dict(kernel=_lib.KDA_KERNEL_SINGLE),
+              dict(sigmoid=_lib.KDA_SIGMOID_TANH), dict(reserved=1), dict(inverse=5)):
+        assert call_scan(**ws, options=_opts(**o)) == _lib.KDA_ERR_OPTION, o
+    for o in (dict(kernel=_lib.KDA_KERNEL_CHUNKED), dict(inverse=_lib.KDA_INVERSE_NEUMANN), dict()):
+        # packed mode with no sequence: valid options pass, nothing is launched
+        assert call_scan(**ws, cu=BADDR[9], num_seqs=0, options=_opts(**o)) == _lib.KDA_OK, o
+
+
+def test_binding_rejects_unknown_option_names():
+    with pytest.raises(ValueError, match="kernel"):
+        kda.fwd_kernel(5, kernel="simt")
+    with pytest.raises(ValueError, match="sigmoid"):
+        kda.fwd_kernel(5, sigmoid="logistic")
 
 
 def test_empty_token_tensors_may_be_null():
