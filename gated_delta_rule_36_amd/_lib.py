@@ -7,8 +7,10 @@ import os
 LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
 # Every symbol include/kda.h declares.
-EXPORTS = ("kda_fwd", "kda_fwd_ex", "kda_fwd_scan", "kda_fwd_scan_workspace_bytes",
-           "kda_status_string", "kda_fwd_kernel", "kda_abi_version")
+EXPORTS = ("kda_fwd", "kda_fwd_ex", "kda_fwd_scan", "kda_fwd_scan_static",
+           "kda_fwd_scan_workspace_bytes", "kda_status_string", "kda_fwd_kernel",
+           "kda_abi_version")
+SCAN_STATIC_BYTES = 32 << 20  # KDA_SCAN_STATIC_BYTES
 ABI_VERSION = 4
 
 # kda_status codes (include/kda.h)
@@ -70,6 +72,9 @@ def load() -> ctypes.CDLL:
     lib.kda_fwd_scan.argtypes = [p, p, p, p, p, d, p, p, p, d, p, ctypes.c_int, p, ctypes.c_int,
                                  p, i64, i64, i64, i64, i64, i64, i64, p, i64, opt, p]
     lib.kda_fwd_scan.restype = ctypes.c_int
+    lib.kda_fwd_scan_static.argtypes = [p, p, p, p, p, d, p, p, p, d, p, ctypes.c_int, p,
+                                        ctypes.c_int, p, i64, i64, i64, i64, i64, i64, i64, opt, p]
+    lib.kda_fwd_scan_static.restype = ctypes.c_int
     lib.kda_fwd_scan_workspace_bytes.argtypes = [p, i64, i64, i64, i64, i64]
     lib.kda_fwd_scan_workspace_bytes.restype = i64
     lib.kda_status_string.argtypes = [ctypes.c_int]

@@ -242,13 +242,15 @@ extern "C" int64_t kda_fwd_scan_workspace_bytes(const int64_t *cu_seqlens, int64
 
 namespace {
 
-// kda_fwd_scan's checks and launch.
+// kda_fwd_scan's checks and launch, with the workspace given (workspace !=
+// nullptr) or, for the static variant, taken from the library's fixed
+// scratch (workspace == nullptr, capacity = its size).
 kda_status fwd_scan(const void *q, const void *k, const void *v, const void *g, const void *beta,
                     double scale, void *out, const float *A_log, const float *dt_bias,
                     double lower_bound, const void *initial_state, kda_dtype initial_state_dtype,
                     void *final_state, kda_dtype final_state_dtype, const int64_t *cu_seqlens,
                     int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
-                    int64_t seg_chunks, void *workspace, int64_t workspace_bytes,
+                    int64_t seg_chunks, void *workspace, int64_t workspace_bytes, bool use_static,
                     const kda_options *options, void *stream)
 {
     Checked c;
@@ -271,15 +273,24 @@ kda_status fwd_scan(const void *q, const void *k, const void *v, const void *g, 
         (n_seg > 2 && c.chains > INT32_MAX / 8))
         return KDA_ERR_SIZE;
     const int64_t need = blocks * 2 * kSlabBytes;
-    if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
-        return KDA_ERR_WORKSPACE;
-    const Span sw = span(workspace, need);
-    for (int i = 0; i < c.n_spans; ++i) {
-        if (sw.overlaps(c.spans[i]))
+    if (use_static) {
+        if (need > kda::kStaticScratchBytes)
             return KDA_ERR_WORKSPACE;
+        if (c.chains == 0)
+            return KDA_OK;
+        if (kda::static_scratch(&workspace) != hipSuccess)
+            return KDA_ERR_LAUNCH;
+    } else {
+        if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+            return KDA_ERR_WORKSPACE;
+        const Span sw = span(workspace, need);
+        for (int i = 0; i < c.n_spans; ++i) {
+            if (sw.overlaps(c.spans[i]))
+                return KDA_ERR_WORKSPACE;
+        }
+        if (c.chains == 0)
+            return KDA_OK;
     }
-    if (c.chains == 0)
-        return KDA_OK;
     kda::FwdParams &p = c.p;
     p.seg_chunks = seg_chunks;
     p.n_seg = n_seg;
@@ -304,7 +315,22 @@ extern "C" kda_status kda_fwd_scan(const void *q, const void *k, const void *v, 
 {
     return fwd_scan(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
                     initial_state_dtype, final_state, final_state_dtype, cu_seqlens, num_seqs, B, T,
-                    H, K, V, seg_chunks, workspace, workspace_bytes, options, stream);
+                    H, K, V, seg_chunks, workspace, workspace_bytes, false, options, stream);
+}
+
+extern "C" kda_status kda_fwd_scan_static(const void *q, const void *k, const void *v, const void *g,
+                                          const void *beta, double scale, void *out,
+                                          const float *A_log, const float *dt_bias, double lower_bound,
+                                          const void *initial_state, kda_dtype initial_state_dtype,
+                                          void *final_state, kda_dtype final_state_dtype,
+                                          const int64_t *cu_seqlens, int64_t num_seqs, int64_t B,
+                                          int64_t T, int64_t H, int64_t K, int64_t V,
+                                          int64_t seg_chunks, const kda_options *options,
+                                          void *stream)
+{
+    return fwd_scan(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+                    initial_state_dtype, final_state, final_state_dtype, cu_seqlens, num_seqs, B, T,
+                    H, K, V, seg_chunks, nullptr, 0, true, options, stream);
 }
 
 extern "C" const char *kda_status_string(kda_status status)

@@ -78,6 +78,13 @@ hipError_t launch_decode(const FwdParams &p, hipStream_t stream);
 // recurrent kernel by default; up to one chunk (16 tokens), the single-chunk
 // kernel; longer or packed calls, the pipelined chunked kernel.
 constexpr int64_t kRecurrentMaxTokens = 8;
+// Bytes of the fixed device scratch kda_fwd_scan_static uses instead of a
+// caller workspace (KDA_SCAN_STATIC_BYTES in kda.h).
+constexpr int64_t kStaticScratchBytes = int64_t(32) << 20;
+// Device address of that scratch on the current device (looked up once per
+// device with hipGetSymbolAddress).
+hipError_t static_scratch(void **ptr);
+
 // The combine step of the segmented form: for every chain and s >= 1,
 // seg_b[c][s] <- M_s seg_b[c][s-1] + seg_b[c][s] (in stored [V][K] terms).
 hipError_t launch_scan_combine(const FwdParams &p, hipStream_t stream);

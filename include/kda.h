@@ -241,6 +241,34 @@ kda_status kda_fwd_scan(const void *q, const void *k, const void *v, const void 
                         const kda_options *options, void *stream);
 
 /*
+ * kda_fwd_scan_static - kda_fwd_scan without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  The scratch the
+ * segmented form needs (kda_fwd_scan_workspace_bytes() for these sizes) is
+ * taken from a fixed device array of the library, KDA_SCAN_STATIC_BYTES per
+ * GPU, which each GPU the library runs on holds until the process ends; the
+ * call itself allocates nothing.  Calls whose scratch would exceed it return
+ * KDA_ERR_WORKSPACE (nothing enqueued); the automatic segment length of the
+ * Python binding keeps about 256 (chain, segment) pairs, i.e. 32 MiB.
+ * Every call on one GPU shares that GPU's array: calls that may overlap on
+ * one GPU (different streams, or different host threads without ordering)
+ * race on it and give wrong results; calls ordered on one stream are safe.
+ * Nothing in the array needs to start at zero (each call writes every slab
+ * before reading it).  Same arguments (minus the workspace), results and
+ * other errors as kda_fwd_scan; KDA_ERR_LAUNCH if the array's device address
+ * cannot be looked up on the current device.
+ */
+#define KDA_SCAN_STATIC_BYTES (32ll << 20)
+kda_status kda_fwd_scan_static(const void *q, const void *k, const void *v, const void *g,
+                               const void *beta, double scale, void *out,
+                               const float *A_log, const float *dt_bias, double lower_bound,
+                               const void *initial_state, kda_dtype initial_state_dtype,
+                               void *final_state, kda_dtype final_state_dtype,
+                               const int64_t *cu_seqlens, int64_t num_seqs,
+                               int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+                               int64_t seg_chunks, const kda_options *options, void *stream);
+
+/*
  * Bytes of workspace kda_fwd_scan needs for these sizes: two fp32 128x128
  * slabs per (chain, segment), with ceil(ceil(T/16) / seg_chunks) segments per
  * chain (every sequence has at most T tokens).  cu_seqlens is only tested for

@@ -182,6 +182,33 @@ def test_scan_argument_errors_are_reported_before_launch(kw, code):
     assert call_scan(**args, **over) == code
 
 
+def call_static(seg=4, **over):
+    a = dict(q=BADDR[0], k=BADDR[1], v=BADDR[2], g=BADDR[3], beta=BADDR[4], scale=0.1,
+             out=BADDR[5], A_log=BADDR[6], dt_bias=BADDR[7], lower_bound=-5.0,
+             init=None, init_dtype=0, final=None, final_dtype=0, cu=None, num_seqs=0,
+             B=1, T=0, H=1, K=128, V=128)
+    a.update(over)
+    return _lib.load().kda_fwd_scan_static(
+        a["q"], a["k"], a["v"], a["g"], a["beta"], a["scale"], a["out"], a["A_log"], a["dt_bias"],
+        a["lower_bound"], a["init"], a["init_dtype"], a["final"], a["final_dtype"], a["cu"],
+        a["num_seqs"], a["B"], a["T"], a["H"], a["K"], a["V"], seg, a.get("options"), None)
+
+
+def test_scan_static_host_checks():
+    """kda_fwd_scan_static: the argument and option checks of kda_fwd_scan,
+    and scratch beyond KDA_SCAN_STATIC_BYTES refused, all before the
+    library's array is looked up or anything is enqueued."""
+    tb = 1 << 44  # fake addresses 16 TiB apart, never dereferenced
+    fake = {n: (i + 1) * tb for i, n in enumerate(["q", "k", "v", "g", "beta", "out", "A_log", "dt_bias"])}
+    # 4 chains x 66 segments x 128 KiB = 33 MiB > 32 MiB
+    assert call_static(seg=1, T=16 * 66, H=4, **fake) == _lib.KDA_ERR_WORKSPACE
+    assert call_static(seg=0) == _lib.KDA_ERR_SIZE
+    assert call_static(K=64) == _lib.KDA_ERR_HEAD_DIM
+    assert call_static(options=_opts(sigmoid=_lib.KDA_SIGMOID_TANH)) == _lib.KDA_ERR_OPTION
+    # no chain: nothing to do, no lookup
+    assert call_static(cu=BADDR[9], num_seqs=0) == _lib.KDA_OK
+
+
 def test_scan_combine_grid_limit():
     """With more than two segments the combine step runs 8 blocks per chain:
     more than INT32_MAX / 8 chains is a size error, reported before the
