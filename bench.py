@@ -10,11 +10,15 @@ one; ``config.kernel`` names it.
 
 The headline workload is the large throughput case: B=8, T=16384, H=32,
 K=V=128, lower_bound=-5, scale=1/sqrt(128), fp32 final_state written, no
-initial state, timed back to back.  By default the same run then measures
+initial state, timed back to back.  By default the same run also measures
 the four other configured workloads (tiny B1 T64 H2, small B2 T128 H8, long
 B1 T8192 H16 with fp32 states, packed varlen N8 H32 with bf16 states), each
 with the cache flushed before every launch (they fit in, or overlap, the
-256 MiB MALL), and reports them under ``configs``.  Prints one JSON line:
+256 MiB MALL), and reports them under ``configs``.  Order: those four first,
+then the headline (its --warmup steps, then its --steps timed steps), then
+every CPU-oracle baseline, so that all GPU timing happens under steady load
+(from idle, the clocks take about 25 launches of the headline to ramp up).
+Prints one JSON line:
 
   value     head-tokens/s of the whole job (B*T*H per step / seconds per step)
   roofline  the kernel against HBM: algorithmic bytes per launch (inputs read
@@ -273,6 +277,35 @@ def main():
     del src, dst
     flush_buf = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
 
+    # The four other configured workloads first (GPU timing only; their CPU
+    # baselines come after all GPU work): every launch is measured with the
+    # cache flushed before it, and the GPU is under steady load when the
+    # headline's own warm-up starts (from idle, the clocks take about 25
+    # launches of the headline workload to ramp up).
+    configs = {}
+    others = [] if args.headline_only else [n for n in OTHER_CONFIGS if n != args.workload]
+    drawn = {}
+    for name in others:
+        y = synth.workload(name, device="cuda")
+        yB, yT, yH, _ = y.q.shape
+        yseg = segment_choice(kda, y, "auto")
+        step_ms, lms = measure(kda, y, y.final_dtype, args.steps, args.warmup, flush_buf, yseg, {})
+        rl = roofline_of(y, y.final_dtype, lms)
+        ht = yB * yT * yH
+        configs[name] = {
+            "workload": name, "B": yB, "T": yT, "H": yH, "lower_bound": y.lower_bound,
+            "varlen": y.cu_seqlens is not None,
+            "initial_state": None if y.initial_state is None else str(y.initial_state.dtype),
+            "final_state": None if y.final_dtype is None else str(y.final_dtype),
+            "kernel": "mfma (segmented)" if yseg else kda.fwd_kernel(yT, y.cu_seqlens is not None),
+            "segment_chunks": yseg, "cache_flushed": True, "head_tokens": ht,
+            "ms_per_step": round(step_ms, 4), "head_tokens_per_s": ht / (step_ms / 1e3),
+            "kernel_ms": rl["kernel_ms"], "frac": rl["frac"], "achieved_gbs": rl["achieved"],
+            "bytes_per_launch": rl["bytes_per_launch"]}
+        print(f"[bench] {name}: {step_ms:.4f} ms/step, frac {rl['frac']}", file=sys.stderr, flush=True)
+        drawn[name] = y.to("cpu")  # inputs for the CPU baseline, off the GPU
+        del y
+
     seg = segment_choice(kda, x, args.segment_chunks)
     ms_per_step, launch_ms = measure(kda, x, final_dtype, args.steps, args.warmup,
                                      flush_buf if args.flush_cache else None, seg, opts)
@@ -306,36 +339,11 @@ def main():
         "cache_flushed": bool(args.flush_cache),
     }
     if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(x, rows=2)
-    del x
-
-    if not args.headline_only:
-        configs = {}
-        for name in OTHER_CONFIGS:
-            if name == args.workload:
-                continue
-            y = synth.workload(name, device="cuda")
-            yB, yT, yH, _ = y.q.shape
-            yseg = segment_choice(kda, y, "auto")
-            step_ms, lms = measure(kda, y, y.final_dtype, args.steps, args.warmup, flush_buf, yseg, {})
-            rl = roofline_of(y, y.final_dtype, lms)
-            ht = yB * yT * yH
-            entry = {"workload": name, "B": yB, "T": yT, "H": yH, "lower_bound": y.lower_bound,
-                     "varlen": y.cu_seqlens is not None,
-                     "initial_state": None if y.initial_state is None else str(y.initial_state.dtype),
-                     "final_state": None if y.final_dtype is None else str(y.final_dtype),
-                     "kernel": "mfma (segmented)" if yseg else kda.fwd_kernel(yT, y.cu_seqlens is not None),
-                     "segment_chunks": yseg, "cache_flushed": True, "head_tokens": ht,
-                     "ms_per_step": round(step_ms, 4), "head_tokens_per_s": ht / (step_ms / 1e3),
-                     "kernel_ms": rl["kernel_ms"], "frac": rl["frac"], "achieved_gbs": rl["achieved"],
-                     "bytes_per_launch": rl["bytes_per_launch"]}
-            print(f"[bench] {name}: {step_ms:.4f} ms/step, frac {rl['frac']}", file=sys.stderr,
-                  flush=True)
-            if not args.no_cpu_baseline:
-                entry["cpu_baseline"] = cpu_baseline(y, rows=None, one_thread=False)
-            configs[name] = entry
-            del y
+        for name, y in drawn.items():
+            configs[name]["cpu_baseline"] = cpu_baseline(y, rows=None, one_thread=False)
+    if configs:
         result["configs"] = configs
     print(json.dumps(result), flush=True)
 
