@@ -1169,12 +1169,12 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
     // The stage ring holds three chunks: iteration `it` starts the loads of
     // chunk it + 2, runs the gate stage on chunk it and, before the barrier,
     // waits for the loads of chunk it + 1 (issued one iteration earlier), so
-    // every chunk has two iterations to arrive.  Past the last chunk the stage
-    // runs on a repeat of it and fills only ring slots that no later stage
-    // reads.  Waves 4-7 load rows 8 (gc16 % 2) .. + 7 of q (waves 4, 5) or k
-    // (6, 7); waves 8-11 load nothing.  The state and solve waves (priority
-    // 3) sit on the critical path; the gate waves fill the issue slots they
-    // leave.
+    // every chunk has two iterations to arrive.  Past the last chunk the
+    // iterations that drain the pipeline load and gate nothing (the state
+    // waves then have the SIMDs to themselves).  Waves 4-7 load rows
+    // 8 (gc16 % 2) .. + 7 of q (waves 4, 5) or k (6, 7); waves 8-11 load
+    // nothing.  The state and solve waves (priority 3) sit on the critical
+    // path; the gate waves fill the issue slots they leave.
     // Fused, waves 8-9 load the rows of k (q is not needed).
     __builtin_amdgcn_s_setprio(1);
     const int tensor = kFused ? 1 : gc16 >> 1;  // 0: q, 1: k
@@ -1191,19 +1191,30 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
     wait_vmem<2>();  // chunk 0 (a no-op for the waves that load nothing)
     lds_barrier();
     uint32_t o3 = 0, o5 = 0;  // chunk it's stage slot and Qt / Kbar slot
-    for (int it = 0; it < n_iter; ++it) {
+    auto gate = [&](int it) {
+        gw.template gate_stage<SIG, kOut>(it, o3, o5);
+        if constexpr (kFused)
+            gw2.template gate_stage<SIG, false>(it, o3, o5);
+        o3 = o3 == 2 * (3 * kTile) ? 0 : o3 + 3 * kTile;
+        o5 = o5 == 4 * kTile ? 0 : o5 + kTile;
+    };
+    int it = 0;
+    for (; it < nc - 2; ++it) {
         // slot of chunk it + 2 (stage: last read by the gate stage of chunk
         // it - 1; V: by WY of chunk it - 4, both before the last barrier)
         if (loads) {
             ld.issue();
             ld.advance(nc);
         }
-        gw.template gate_stage<SIG, kOut>(it, o3, o5);
-        if constexpr (kFused)
-            gw2.template gate_stage<SIG, false>(it, o3, o5);
-        o3 = o3 == 2 * (3 * kTile) ? 0 : o3 + 3 * kTile;
-        o5 = o5 == 4 * kTile ? 0 : o5 + kTile;
+        gate(it);
         wait_vmem<2>();  // chunk it + 1
+        lds_barrier();
+    }
+    // the last two chunks (nothing left to load), then the drain
+    for (; it < n_iter; ++it) {
+        if (it < nc)
+            gate(it);
+        wait_vmem<0>();  // chunk nc - 1 (first pass only; later a no-op)
         lds_barrier();
     }
     // no load may still be writing LDS when the wave ends
