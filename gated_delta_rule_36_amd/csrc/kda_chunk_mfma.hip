@@ -155,7 +155,7 @@ struct __align__(16) SharedPipe {
     uint16_t pmat[4][C][C];    // P (bf16), lower
     uint16_t tb_hi[2][C][C];   // T diag(beta) = hi + lo, two bf16 parts
     uint16_t tb_lo[2][C][C];
-    uint16_t w_row[2][C][kWPitch];  // W, token-major, padded rows
+    uint16_t w_row[2][C][kWPitch];  // -W, token-major, padded rows
     float ut[2][D][C];         // U~, column-major
     uint16_t stage[3][3][C][D];  // q, k, g as loaded (DMA), token-major; read by the gate stage
 };
@@ -696,7 +696,8 @@ struct SolveWave {
 
     // WY: W and U~ for channels / value columns 32 pw .. 32 pw + 31 of chunk x.
     // T diag(beta) = T_hi + T_lo (two bf16 parts) enters one 16x16x32 MFMA
-    // as the contraction [T_hi | T_lo] against [X; X].
+    // as the contraction [T_hi | T_lo] against [X; X].  The W tile receives
+    // -W, so that the state waves accumulate U = U~ - W S onto U~.
     __device__ __forceinline__ void wy_stage(int x) const
     {
         const uint32_t s2 = x & 1, s4 = x & 3, s6 = x % 6;
@@ -711,10 +712,10 @@ struct SolveWave {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const u32x2_t ka = lds_ld<u32x2_t>(ak + 32 * C * t);
-            // lane (token l16, g4): W[l16][32pw+16t+4g4+i], stored at chunk
-            // 4 pw + g4, half t of the padded row
+            // lane (token l16, g4): W[l16][32pw+16t+4g4+i], stored negated at
+            // chunk 4 pw + g4, half t of the padded row
             const f32x4_t w = mfma32(cat8(ka, ka), t8, zero);
-            lds_st(aw + 8 * t, pack_bf16x4(w));
+            lds_st(aw + 8 * t, pack_bf16x4(-w));
             const u32x2_t vb = lds_tr(av[t]);
             // lane (vcol, g4): U~[4g4+i][vcol]
             const f32x4_t u = mfma32(t8, cat8(vb, vb), zero);
@@ -745,7 +746,7 @@ struct StateWave {
     int n_full, tail;          // full chunks of the range; length of a partial last chunk
     char *out_base;            // out at the range's first token, value column 32 w (wave-uniform)
     int64_t out_chunk_bytes;   // between consecutive chunks of out: C * H * 256
-    uint32_t out_lane;         // lane offset: token l16, value column 8 g4
+    uint32_t out_lane;         // lane offset: token l16, value column 4 g4
     // LDS addresses (ring slot 0) of this lane's reads: Qt operands
     // (tok_lane), W row l16 chunk g4, U~ column 32 w + l16, P row l16,
     // Gamma_C rows 4 g4 .., Kbar channel l16.
@@ -822,16 +823,22 @@ struct StateWave {
         const uint32_t s2 = x & 1, s4 = x & 3;
         const int len = x < n_full ? C : tail;
 
-        // X = W S (lane (vcol, g4): rows 4g4..4g4+3) and Y^T = S^T Qt^T (lane
-        // (token, g4): value columns 4g4..4g4+3 of the tile), from the same
-        // operand registers with the roles of A and B swapped.  S enters as
-        // bf16 B operands: contraction slot 8*g4 + e maps to state row
-        // 32kt + 4g4 + e (e < 4) and 32kt + 16 + 4g4 + (e - 4) (e >= 4), which
-        // is exactly what this lane's accumulators of tiles 2kt, 2kt+1 hold
-        // and what chunk 4 kt + g4 of a W row holds.
+        // U = U~ - W S (lane (vcol, g4): rows 4g4..4g4+3), accumulated onto
+        // U~ from the W tile's -W (U = -W S without v: the transition), and
+        // Y^T = S^T Qt^T (lane (token, g4): value columns 4g4..4g4+3 of the
+        // tile), from the same operand registers with the roles of A and B
+        // swapped.  S enters as bf16 B operands: contraction slot 8*g4 + e
+        // maps to state row 32kt + 4g4 + e (e < 4) and 32kt + 16 + 4g4 + (e - 4)
+        // (e >= 4), which is exactly what this lane's accumulators of tiles
+        // 2kt, 2kt+1 hold and what chunk 4 kt + g4 of a W row holds.
         const uint32_t aw = slot_base(rd_w + s2 * kTileW), aq = slot_base(rd_q + o5);
         f32x4_t X[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         f32x4_t Y[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        if constexpr (MODE != kChunkTransition) {
+            const uint32_t au = slot_base(rd_u + s2 * kTileU);
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) X[nt] = lds_ld<f32x4_t>(au + 64 * C * nt);
+        }
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
             const bf16x8_t wa = __builtin_bit_cast(bf16x8_t, lds_ld<u32x4_t>(aw + 64 * kt));
@@ -845,33 +852,21 @@ struct StateWave {
             }
         }
 
-        // U = U~ - W S, as bf16 operands (lane (vcol, g4): tokens 4g4..4g4+3)
-        u32x2_t ub[2];
-        if constexpr (MODE == kChunkTransition) {
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) ub[nt] = pack_bf16x4(-X[nt]);
-        } else {
-            const uint32_t au = slot_base(rd_u + s2 * kTileU);
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) ub[nt] = pack_bf16x4(lds_ld<f32x4_t>(au + 64 * C * nt) - X[nt]);
-        }
+        // U as bf16 operands (lane (vcol, g4): tokens 4g4..4g4+3)
+        const u32x2_t ub[2] = {pack_bf16x4(X[0]), pack_bf16x4(X[1])};
 
         if constexpr (kOut) {
             // O^T = Y^T + U^T P^T; lane (token l16, g4) then holds 4
-            // consecutive output values of its token
+            // consecutive output values of its token in each tile: value
+            // columns 16 nt + 4 g4 .. + 3, one 8-byte store per tile
             const u32x2_t pa = lds_ld<u32x2_t>(slot_base(rd_p + s4 * kTileCC));
             const u32x2_t o0 = pack_bf16x4(mfma16(ub[0], pa, Y[0]));
             const u32x2_t o1 = pack_bf16x4(mfma16(ub[1], pa, Y[1]));
-            // regroup across the 16-lane rows so that lane (l16, g4) holds
-            // value columns 8 g4 .. 8 g4 + 7 of its token: one 16-byte store
-            uint32_t a0 = o0[0], a1 = o0[1], b0 = o1[0], b1 = o1[1];
-            swap_rows32(a0, b0);
-            swap_rows32(a1, b1);
-            swap_rows16(a0, b0);
-            swap_rows16(a1, b1);
-            if (l16 < len)
-                *reinterpret_cast<u32x4_t *>(out_base + int64_t(x) * out_chunk_bytes + out_lane) =
-                    u32x4_t{a0, a1, b0, b1};
+            if (l16 < len) {
+                char *const o = out_base + int64_t(x) * out_chunk_bytes + out_lane;
+                *reinterpret_cast<u32x2_t *>(o) = o0;
+                *reinterpret_cast<u32x2_t *>(o + 32) = o1;
+            }
         }
 
         // S <- diag(Gamma_C) S + Kbar^T U
@@ -1008,7 +1003,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
         StateWave<PipeLayout> sw{p, w, lane, l16, g4, n_full, tail,
                                   reinterpret_cast<char *>(p.out + first * D + 32 * w),
                                   C * tok_bytes,
-                                  static_cast<uint32_t>(l16 * tok_bytes + 16 * g4),
+                                  static_cast<uint32_t>(l16 * tok_bytes + 8 * g4),
                                   sh0 + kOffQt + tok_lane(l16, g4),
                                   sh0 + kOffW + 2 * kWPitch * l16 + 16 * g4,
                                   sh0 + kOffU + 128 * C * w + row32_lane(l16, g4),
@@ -1257,7 +1252,7 @@ __global__ __launch_bounds__(256, 4) void chunk_single_kernel(FwdParams p)
     StateWave<SL> sw{p, wave, lane, l16, g4, n_full, tail,
                      reinterpret_cast<char *>(p.out + first * D + 32 * wave),
                      C * tok_bytes,
-                     static_cast<uint32_t>(l16 * tok_bytes + 16 * g4),
+                     static_cast<uint32_t>(l16 * tok_bytes + 8 * g4),
                      sh0 + SL::kOffQt + tok_lane(l16, g4),
                      sh0 + SL::kOffW + 2 * kWPitch * l16 + 16 * g4,
                      sh0 + SL::kOffU + 128 * C * wave + row32_lane(l16, g4),

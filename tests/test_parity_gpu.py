@@ -236,10 +236,12 @@ def test_large_workload_parity_all_chains():
 # --------------------------------------------------------------------------
 
 @pytest.mark.parametrize("kernel", [None, "mfma"])
-@pytest.mark.parametrize("T", [0, 1, 15, 16, 17, 33, 100])
+@pytest.mark.parametrize("T", [0, 1, 15, 16, 17, 32, 33, 48, 49, 100])
 def test_chunk_edges(T, kernel, options):
     """Short calls take the recurrent kernel by default; kernel="mfma"
-    keeps the chunked kernel covered on the same shapes."""
+    keeps the chunked kernel covered on the same shapes: one to four chunks,
+    full or with a tail (the pipelined kernel loads two chunks ahead and
+    stops loading for the last two)."""
     if kernel:
         options(kernel=kernel)
     print(f"[case] chunk edge T={T} kernel={kernel or 'default'}", flush=True)
