@@ -28,10 +28,12 @@
  *
  * Ownership and threading: the caller owns every buffer.  All tensor
  * pointers are DEVICE pointers to contiguous row-major memory on the current
- * HIP device.  The library allocates nothing, keeps no state between calls,
- * reads no environment variables, never synchronises and is safe to call
- * from several host threads.  The work is enqueued on `stream` (a
- * hipStream_t; NULL = the default stream) and completes asynchronously.
+ * HIP device.  The library allocates nothing, reads no environment
+ * variables, never synchronises and is safe to call from several host
+ * threads; apart from kda_fwd_scan_static (one fixed scratch array per GPU,
+ * shared by its calls, see there) it keeps no state between calls.  The
+ * work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ * and completes asynchronously.
  */
 #ifndef KDA_H
 #define KDA_H
