@@ -364,10 +364,18 @@ __device__ __forceinline__ uint32_t gload_u16(const char *p)
 // read at base + voff, land at LDS byte address dst + 16 i (dst is
 // wave-uniform and goes in M0).  Written as asm so that the compiler does not
 // make later, unrelated LDS accesses wait for it; the issuing wave waits
-// (vmcnt) before the barrier that hands the data to the other waves.
+// (vmcnt) before the barrier that hands the data to the other waves.  NT:
+// the non-temporal hint (nt), for inputs read for the last time (a whole
+// chain, or the segmented form's output pass); the map passes of the
+// segmented form leave it off, since their inputs are read again by the
+// output pass and may still be in the last-level cache then.
+template <bool NT>
 __device__ __forceinline__ void dma16(const char *base, uint32_t voff, uint32_t dst)
 {
-    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(dst) : "memory");
+    if constexpr (NT)
+        asm volatile("global_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(base), "{m0}"(dst) : "memory");
+    else
+        asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(dst) : "memory");
 }
 
 // Direct loads of 4 NJ token rows of one tensor per chunk into an LDS ring,
@@ -377,7 +385,8 @@ __device__ __forceinline__ void dma16(const char *base, uint32_t voff, uint32_t 
 // data.  The cursor (chunk, source, ring slot) advances one chunk per
 // iteration up to the last chunk, so the loop needs no per-chunk multiplies
 // or remainders.  Bases and strides are wave-uniform (scalar registers).
-template <int NJ>
+// NT: the non-temporal hint on the loads (dma16).
+template <int NJ, bool NT = true>
 struct Loader {
     const char *src;              // the tensor at chunk x
     int64_t chunk_bytes;          // between consecutive chunks: C * H * 256
@@ -409,7 +418,7 @@ struct Loader {
     {
         const bool f = x < n_full;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) dma16(src, f ? full[j] : tail[j], dst + 1024 * j);
+        for (int j = 0; j < NJ; ++j) dma16<NT>(src, f ? full[j] : tail[j], dst + 1024 * j);
     }
     __device__ __forceinline__ void advance(int nc)
     {
@@ -1092,7 +1101,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
             // wave also loads all 16 rows of g and v two chunks ahead (g into
             // the stage ring, v into its ring for WY), like the gate waves'
             // loads of q and k.  Without outputs P is not needed.
-            Loader<4> lg, lv;
+            Loader<4, kOut> lg, lv;
             lg.init(p.g + first * D, tok_bytes, 0, lane, tail, n_full, sh0 + kOffStage + 2 * kTile, 3 * kTile, 3);
             lv.init(p.v + first * D, tok_bytes, 0, lane, tail, n_full, sh0 + kOffV, kTile, 6);
             if (n_iter > 0) {
@@ -1174,7 +1183,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(FwdParams p)
     __builtin_amdgcn_s_setprio(1);
     const int tensor = kFused ? 1 : gc16 >> 1;  // 0: q, 1: k
     const bool loads = kFused ? gc16 < 2 : gc16 < 4 && (kOut || gc16 >= 2);  // q only for the output
-    Loader<2> ld;
+    Loader<2, kOut> ld;
     ld.init((tensor == 0 ? p.q : p.k) + first * D, tok_bytes, 8 * (gc16 & 1), lane, tail, n_full,
             sh0 + kOffStage + tensor * kTile, 3 * kTile, 3);
     if (loads) {
