@@ -987,3 +987,57 @@ def test_graph_capture_replays(T, seg, kernel):
     ro, rf = oracle_of(x)
     assert_close(f"graph {kernel} out", out.double().cpu().numpy(), ro)
     assert_close(f"graph {kernel} final", fin.double().cpu().numpy(), rf)
+
+
+# --------------------------------------------------------------------------
+# Seeded sweep: random shapes, packed lengths, gate bounds, state dtypes and
+# the library's kernels and forms, each checked against the oracle.
+# --------------------------------------------------------------------------
+
+SWEEP_STATES = [(None, None), (None, torch.bfloat16), (None, torch.float32),
+                (torch.bfloat16, torch.bfloat16), (torch.float32, torch.float32),
+                (torch.float32, None), (torch.bfloat16, None)]
+
+
+def sweep_case(i):
+    """Case i of the sweep: a plain description of one call (seeded)."""
+    import random
+    rng = random.Random(1000 + i)
+    varlen = rng.random() < 0.4
+    H = rng.randint(1, 6)
+    lb = rng.choice([-5.0, -3.0, -0.5, 0.0, round(rng.uniform(-5.0, 0.0), 3)])
+    init, final = rng.choice(SWEEP_STATES)
+    if varlen:
+        lens = [rng.choice([0, 1, 15, 16, 17, rng.randint(0, 300)]) for _ in range(rng.randint(1, 4))]
+        B, T = 1, sum(lens)
+    else:
+        lens = None
+        B = rng.randint(1, 3)
+        T = rng.choice([0, 1, rng.randint(2, 16), rng.randint(17, 64), rng.randint(65, 400)])
+    form = rng.choice(["auto", "mfma", "recurrent", "single", "neumann", "tanh", "segmented"])
+    if form == "single" and (varlen or T > 16):
+        form = "auto"
+    seg = rng.randint(1, 4) if form == "segmented" else None
+    return dict(B=B, T=T, H=H, lens=lens, lb=lb, init=init, final=final, form=form, seg=seg,
+                seed=2000 + i)
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_seeded_sweep(i, options):
+    c = sweep_case(i)
+    print(f"[case] sweep {i}: {c}", flush=True)
+    form = c["form"]
+    if form in ("mfma", "recurrent", "single"):
+        options(kernel=form)
+    elif form == "neumann":
+        options(inverse="neumann")
+    elif form == "tanh":
+        options(sigmoid="tanh")
+    x = synth.make_inputs(c["B"], c["T"], c["H"], lower_bound=c["lb"], seed=c["seed"],
+                          seq_lengths=c["lens"], init_dtype=c["init"], device="cuda")
+    o, f = run_gpu(x, c["final"], segment_chunks=c["seg"])
+    ro, rf = oracle_of(x)
+    if c["T"]:
+        assert_close(f"sweep {i} out", o, ro)
+    if f is not None:
+        assert_close(f"sweep {i} final", f, rf)
