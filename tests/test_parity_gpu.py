@@ -942,6 +942,41 @@ def test_max_heads(T, kernel):
     check_all_chains(f"max heads T={T}", x, out, None, batch=8192)
 
 
+def test_tensors_beyond_4gib():
+    """B=8, T=2^20, H=4: every input tensor is 8 GiB, so the last batch
+    row's tokens sit more than 7 GiB into it (64-bit offsets everywhere).
+    The first 2048 tokens of rows 0 and 7 (all heads) against the oracle, and
+    row 7 as a whole (out and final state, all 2^20 tokens) bit for bit
+    against the same row run on its own from low addresses."""
+    B, T, H = 8, 1 << 20, 4
+    print(f"[case] beyond 4 GiB: B={B} T={T} H={H} (inputs {4 * B * T * H * 256 >> 30} GiB)", flush=True)
+    x = synth.make_inputs(B, T, H, lower_bound=-5.0, seed=910, device="cuda")
+    out = torch.empty_like(x.v)
+    final = torch.empty(B, H, 128, 128, dtype=torch.float32, device="cuda")
+    fwd(x.q, x.k, x.v, x.g, x.beta, x.scale, out, x.A_log, x.dt_bias, x.lower_bound,
+        final_state=final)
+    torch.cuda.synchronize()
+    n = 2048
+    for row in (0, B - 1):
+        sl = slice(row, row + 1)
+        q, k, v, g, beta = (t[sl, :n].cpu() for t in (x.q, x.k, x.v, x.g, x.beta))
+        ro, _ = kda_oracle(q, k, v, g, beta, x.scale, x.A_log.cpu(), x.dt_bias.cpu(),
+                           x.lower_bound)
+        assert_close(f"beyond 4 GiB row {row} out[:{n}]", out[sl, :n].double().cpu().numpy(), ro)
+    row = B - 1
+    y = synth.KdaInputs(**{**x.__dict__, **{t: getattr(x, t)[row:row + 1].contiguous()
+                                            for t in ("q", "k", "v", "g", "beta")}})
+    del x
+    out1 = torch.empty_like(y.v)
+    final1 = torch.empty(1, H, 128, 128, dtype=torch.float32, device="cuda")
+    fwd(y.q, y.k, y.v, y.g, y.beta, y.scale, out1, y.A_log, y.dt_bias, y.lower_bound,
+        final_state=final1)
+    torch.cuda.synchronize()
+    assert torch.equal(out1[0], out[row]), "row 7: out differs from the same row run alone"
+    assert torch.equal(final1[0], final[row]), "row 7: final state differs"
+    assert torch.isfinite(final).all()
+
+
 # --------------------------------------------------------------------------
 # HIP graph capture (serving loops replay a captured call)
 # --------------------------------------------------------------------------
