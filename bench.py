@@ -30,6 +30,8 @@ Prints one JSON line:
   configs   per other workload: kernel ms, roofline fraction, head-tokens/s
             and the oracle's head-tokens/s on the same inputs (all chains)
   copy_gbs  a plain 1 GiB device-to-device copy on the same GPU, for context
+  launch_ms_stats  the spread of the timed launches (first, min, median, max,
+            first and last quarter means)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--headline-only] [--segment-chunks auto|off|N]
@@ -153,7 +155,8 @@ def cpu_baseline(x, rows=None, one_thread=True):
 
 
 def measure(kda, x, final_dtype, steps, warmup, flush, seg, opts):
-    """Warm up, then time `steps` calls; returns (ms_per_step, mean launch ms).
+    """Warm up, then time `steps` calls; returns (ms_per_step, mean launch ms,
+    the per-launch ms in order).
 
     Per-launch HIP events on the launch stream give the kernel time.  With
     `flush` (a 512 MiB device buffer) it is read before every launch, outside
@@ -193,7 +196,19 @@ def measure(kda, x, final_dtype, steps, warmup, flush, seg, opts):
     mean_launch = sum(launch_ms) / len(launch_ms)
     # with cache flushes in between, the wall clock would count them: use the launches
     ms_per_step = mean_launch if flush is not None else wall * 1e3 / steps
-    return ms_per_step, mean_launch
+    return ms_per_step, mean_launch, launch_ms
+
+
+def launch_stats(launch_ms):
+    """The timed launches' spread: from idle the engine clock needs some 25
+    launches of the large workload to settle, so early and late launches
+    differ (the mean is what `value` and `roofline` use)."""
+    xs = sorted(launch_ms)
+    q = max(1, len(launch_ms) // 4)
+    return {"first": round(launch_ms[0], 4), "min": round(xs[0], 4),
+            "median": round(xs[len(xs) // 2], 4), "max": round(xs[-1], 4),
+            "first_quarter_mean": round(sum(launch_ms[:q]) / q, 4),
+            "last_quarter_mean": round(sum(launch_ms[-q:]) / q, 4)}
 
 
 def roofline_of(x, final_dtype, launch_ms, traffic=None):
@@ -289,7 +304,7 @@ def main():
         y = synth.workload(name, device="cuda")
         yB, yT, yH, _ = y.q.shape
         yseg = segment_choice(kda, y, "auto")
-        step_ms, lms = measure(kda, y, y.final_dtype, args.steps, args.warmup, flush_buf, yseg, {})
+        step_ms, lms, _ = measure(kda, y, y.final_dtype, args.steps, args.warmup, flush_buf, yseg, {})
         rl = roofline_of(y, y.final_dtype, lms)
         ht = yB * yT * yH
         configs[name] = {
@@ -307,8 +322,8 @@ def main():
         del y
 
     seg = segment_choice(kda, x, args.segment_chunks)
-    ms_per_step, launch_ms = measure(kda, x, final_dtype, args.steps, args.warmup,
-                                     flush_buf if args.flush_cache else None, seg, opts)
+    ms_per_step, launch_ms, per_launch = measure(kda, x, final_dtype, args.steps, args.warmup,
+                                                 flush_buf if args.flush_cache else None, seg, opts)
     head_tokens = B * T * H
     print(f"[bench] {args.workload}: {args.warmup} warm-up + {args.steps} timed steps, "
           f"{ms_per_step:.4f} ms/step", file=sys.stderr, flush=True)
@@ -335,6 +350,7 @@ def main():
                    "final_state": None if final_dtype is None else str(final_dtype),
                    "segment_chunks": seg, "kernel": kernel, **opts},
         "roofline": roofline,
+        "launch_ms_stats": launch_stats(per_launch),
         "copy_gbs": round(copy_gbs, 1),
         "cache_flushed": bool(args.flush_cache),
     }

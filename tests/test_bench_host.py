@@ -121,3 +121,11 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "not supported" in r.stderr and r.stdout == ""
+
+
+def test_launch_stats():
+    st = bench.launch_stats([1.4, 1.38, 1.35, 1.33, 1.30, 1.29, 1.28, 1.27])
+    assert st["first"] == 1.4 and st["min"] == 1.27 and st["max"] == 1.4
+    assert st["median"] == 1.33  # the upper median of an even count
+    assert st["first_quarter_mean"] == pytest.approx((1.4 + 1.38) / 2)
+    assert st["last_quarter_mean"] == pytest.approx((1.28 + 1.27) / 2)
